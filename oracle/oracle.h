@@ -1,0 +1,58 @@
+/*
+ * fp64 CPU oracle for draft-block paged attention.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the library path may call, link or load
+ * this; only the tests, the smoke check and the benchmark's CPU-baseline leg
+ * use it. It shares no code with the GPU library.
+ */
+#ifndef ORACLE_H
+#define ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct oracle_params {
+    int32_t batch;             /* B requests */
+    int32_t block_size;        /* K draft queries per request */
+    int32_t num_q_heads;       /* Hq */
+    int32_t num_kv_heads;      /* Hkv, divides Hq */
+    int32_t head_dim;          /* D */
+    int32_t page_size;         /* P tokens per page */
+    int32_t page_table_stride; /* entries per page-table row */
+    int32_t num_pages;         /* pages in each pool; every page id read must lie below it */
+    int32_t window_left;       /* -1: no left limit; W >= 1: keys (p - W, p] on the causal side */
+    int32_t window_right;      /* -1: every later block key; 0: none; > 0: at most that many */
+    double sm_scale;
+} oracle_params;
+
+enum { ORACLE_PART_ALL = 0, ORACLE_PART_CAUSAL = 1, ORACLE_PART_FUTURE = 2 };
+
+/*
+ * Attention of every query row over its key set, straight from the definition.
+ * q: bf16 bits [B, K, Hq, D]; k_pool, v_pool: bf16 bits [pages, Hkv, P, D];
+ * page_table: int32 [B, stride]; seq_lens: int32 [B] (context + K keys).
+ * pairs: optional list of n_pairs (b, h_kv) int32 pairs; when NULL every pair
+ * is computed. out: double [B, K, Hq, D]; lse2: double [B, K, Hq] (base-2
+ * log-sum-exp of the scaled logits). Rows outside the chosen pairs are left
+ * untouched. An empty key set gives out = 0, lse2 = -inf.
+ * Returns 0, or -1 on invalid arguments.
+ */
+int oracle_attention(const oracle_params* prm, int part, const uint16_t* q, const uint16_t* k_pool,
+                     const uint16_t* v_pool, const int32_t* page_table, const int32_t* seq_lens,
+                     const int32_t* pairs, int n_pairs, double* out, double* lse2, int threads);
+
+/* Log-sum-exp merge of two normalised attention results over disjoint key sets. */
+void oracle_merge(int64_t rows, int32_t head_dim, const double* out_a, const double* lse_a, const double* out_b,
+                  const double* lse_b, double* out, double* lse);
+
+/* Exact bf16 -> double widening used by the oracle (exported for its tests). */
+double oracle_bf16_to_double(uint16_t bits);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif
