@@ -1,0 +1,157 @@
+/*
+ * blockattn: draft-block attention over a paged bf16 KV cache, for MI355X (gfx950).
+ *
+ * A speculative-decoding drafter proposes a block of K draft tokens per
+ * request. Each of the K block queries (times the GQA group, so R = K * Hq/Hkv
+ * query rows per KV head) attends to the request's paged context plus the K
+ * block keys, which are already appended to the cache.
+ *
+ *  - blockattn_forward: the non-causal unwindowed form. Every block query of a
+ *    request sees the same N_b = seq_lens[b] keys (TensorRT-LLM PR #20374,
+ *    "non-causal unwindowed DFlash block attention", Description: with no mask
+ *    all block queries attend the same seq_lens_after keys).
+ *  - blockattn_windowed_forward: the non-causal windowed form, served as a
+ *    causal windowed decode that yields a base-2 LSE, followed by a
+ *    log-sum-exp merge of the block keys that follow each query (TensorRT-LLM
+ *    PR #21130, DSpark non-causal windowed draft layer, Description items 1-2).
+ *    With K = 1 or window_right = 0 no block key follows any query, the merge
+ *    is skipped and the causal result is returned as is.
+ *
+ * Definitions (p = N_b - K + i is the absolute position of block query i):
+ *   s_j  = sm_scale * <q[b,i,h,:], k_j>, with k_j read through the page table
+ *   key set, unwindowed: j in [0, N_b)
+ *   key set, windowed:   j in [max(0, p - W + 1), p]  (the causal window, W keys
+ *                        including p) joined with j in (p, min(N_b - 1, p + W_r)]
+ *                        (W_r = -1: every later block key)
+ *   out[b,i,h,:] = sum_j softmax(s)_j v_j,   lse[b,i,h] = log2 sum_j exp(s_j)
+ *
+ * Layouts (all contiguous, row-major, device memory unless stated):
+ *   q, out      bf16 [B, K, Hq, D]
+ *   k_cache,    bf16 [num_pages, Hkv, P, D] each ("HND" pages, PR #20374 sweep
+ *   v_cache          setup); key j of request b is slot j % P of page
+ *                    page_table[b, j / P]
+ *   page_table  int32 [B, page_table_stride]; entries past ceil(N_b / P) are
+ *               never read
+ *   seq_lens    int32 [B] = C_b + K, context plus the appended block
+ *   lse         fp32 [B, K, Hq], base 2
+ *   Query head h uses kv head h / (Hq / Hkv).
+ *
+ * Ownership: the caller owns every device buffer, the workspace and the stream.
+ * The library owns only the plan (a host object). Nothing is allocated on the
+ * device by a forward call, and a forward call never synchronises the host, so
+ * it can be captured in a HIP graph.
+ *
+ * Errors: every entry point returns a blockattn_status. On any error nothing is
+ * launched, and blockattn_last_error() (thread-local) names the offending field
+ * and how to fix it.
+ */
+#ifndef BLOCKATTN_H
+#define BLOCKATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum blockattn_status {
+    BLOCKATTN_OK = 0,
+    BLOCKATTN_ERR_INVALID_ARGUMENT = 1,  /* a shape, length, pointer or window out of range */
+    BLOCKATTN_ERR_UNSUPPORTED = 2,       /* a valid shape this build has no kernel for (D, P, R) */
+    BLOCKATTN_ERR_WORKSPACE_TOO_SMALL = 3,
+    BLOCKATTN_ERR_PLAN_MISMATCH = 4,     /* forward kind or workspace differs from the plan's */
+    BLOCKATTN_ERR_HIP = 5                /* the HIP runtime reported an error */
+} blockattn_status;
+
+typedef struct blockattn_params {
+    int32_t batch;             /* B >= 1 requests */
+    int32_t block_size;        /* K draft queries per request, 1..16 */
+    int32_t num_q_heads;       /* Hq, a multiple of Hkv */
+    int32_t num_kv_heads;      /* Hkv >= 1 */
+    int32_t head_dim;          /* D: 64 or 128 */
+    int32_t page_size;         /* P tokens per page: 16, 32, 64 or 128 */
+    int32_t page_table_stride; /* int32 entries per page-table row, >= ceil(N_b / P) */
+    int32_t num_pages;         /* pages in each pool; page ids must lie in [0, num_pages) */
+    int32_t window_left;       /* -1: unwindowed form; W >= 1: windowed form, causal window of W keys */
+    int32_t window_right;      /* windowed form: -1 every later block key, 0 none, > 0 at most that many.
+                                  Must be -1 for the unwindowed form. */
+    float sm_scale;            /* softmax scale, finite and > 0 (usually 1/sqrt(D)) */
+    int32_t splits_override;   /* 0: automatic split count. > 0: exactly that many KV splits per
+                                  (request, kv head), clamped to the request's 32-token tile count
+                                  (for testing split invariance and tuning) */
+} blockattn_params;
+
+typedef struct blockattn_plan_s* blockattn_plan_t;
+
+typedef struct blockattn_plan_info {
+    int32_t kind;              /* 0 unwindowed, 1 windowed */
+    int32_t units;             /* work units (workgroups) of the split-KV partial kernel */
+    int32_t max_splits;        /* largest split count of any (request, kv head) */
+    int32_t merge_active;      /* 1 when the windowed future-block-key merge runs */
+    int32_t waves_per_unit;    /* wavefronts per workgroup of the partial kernel */
+    int32_t token_groups;      /* wavefronts streaming different tiles inside one workgroup */
+    int32_t row_waves;         /* wavefronts sharing one tile, each owning some query rows */
+    int32_t uploaded;          /* 1 once the work list has been copied into a workspace */
+    size_t workspace_bytes;    /* bytes the plan needs */
+} blockattn_plan_info_t;
+
+/*
+ * Exact workspace bytes needed for these parameters and host lengths: the
+ * split-KV work list, the per-(request, kv head) table and the fp32 partial
+ * softmax states (acc, m, l) of every work unit.
+ * seq_lens_host: int32 [B] on the host. Returns BLOCKATTN_OK and sets *bytes.
+ */
+int blockattn_workspace_size(const blockattn_params* params, const int32_t* seq_lens_host, size_t* bytes);
+
+/*
+ * Validate, choose the split-KV decomposition for gfx950 and lay out the
+ * workspace. seq_lens_host fixes the split counts; forward reads the live
+ * lengths from device memory, so the lengths may change between forwards (for
+ * example under graph replay) as long as every N_b stays in
+ * [K, page_table_stride * P].
+ * workspace: device buffer of workspace_bytes, or NULL for a host-only plan
+ * (info and validation only; such a plan cannot run). With a workspace, one
+ * asynchronous host-to-device copy of the work list is enqueued on stream
+ * (a hipStream_t, NULL = default stream). The plan must outlive that copy;
+ * blockattn_plan_destroy waits for it.
+ * On success *plan holds a new plan owned by the caller.
+ */
+int blockattn_plan(const blockattn_params* params, const int32_t* seq_lens_host, void* workspace,
+                   size_t workspace_bytes, void* stream, blockattn_plan_t* plan);
+
+/*
+ * Non-causal unwindowed block attention (the plan must have window_left = -1).
+ * q, k_cache, v_cache: bf16 device buffers (layouts above); page_table,
+ * seq_lens: int32 device buffers; workspace: the buffer given to the plan;
+ * out: bf16 [B, K, Hq, D]; lse: fp32 [B, K, Hq] or NULL; stream: hipStream_t.
+ * Launch only: no allocation, no host synchronisation.
+ */
+int blockattn_forward(blockattn_plan_t plan, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* page_table, const int32_t* seq_lens, void* workspace, void* out, float* lse,
+                      void* stream);
+
+/*
+ * Non-causal windowed block attention (the plan must have window_left >= 1):
+ * a causal windowed split-KV decode, its combine, and the fused merge of the
+ * block keys after each query. Same arguments as blockattn_forward; lse is
+ * required and receives the final, merged base-2 LSE.
+ */
+int blockattn_windowed_forward(blockattn_plan_t plan, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* page_table, const int32_t* seq_lens, void* workspace, void* out,
+                               float* lse, void* stream);
+
+/* Describe the plan (path taken, units, splits, merge on or off). */
+int blockattn_plan_info(blockattn_plan_t plan, blockattn_plan_info_t* info);
+
+/* Wait for the plan's pending work-list copy, then free it. NULL is ignored. */
+void blockattn_plan_destroy(blockattn_plan_t plan);
+
+/* Message of the last error on the calling thread ("" if none). */
+const char* blockattn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BLOCKATTN_H */

@@ -1,0 +1,256 @@
+"""Python binding of the blockattn C ABI (``include/blockattn.h``).
+
+Argument marshalling only: every step of the attention runs in the gfx950
+kernels of ``libblockattn.so``. PyTorch supplies device memory and streams.
+There is no fallback: if the library is not built, importing the entry points
+raises.
+
+The functions carry the C names. Tensors are passed by pointer after a check
+that their dtype, device, contiguity and element count match the plan's
+shapes, so a mismatched buffer is refused on the host instead of reaching a
+kernel.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libblockattn.so")
+
+BLOCKATTN_OK = 0
+BLOCKATTN_ERR_INVALID_ARGUMENT = 1
+BLOCKATTN_ERR_UNSUPPORTED = 2
+BLOCKATTN_ERR_WORKSPACE_TOO_SMALL = 3
+BLOCKATTN_ERR_PLAN_MISMATCH = 4
+BLOCKATTN_ERR_HIP = 5
+
+EXPORTED = (
+    "blockattn_workspace_size",
+    "blockattn_plan",
+    "blockattn_forward",
+    "blockattn_windowed_forward",
+    "blockattn_plan_info",
+    "blockattn_plan_destroy",
+    "blockattn_last_error",
+)
+
+
+class blockattn_params(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("page_table_stride", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("window_left", ctypes.c_int32),
+        ("window_right", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float),
+        ("splits_override", ctypes.c_int32),
+    ]
+
+
+class blockattn_plan_info_t(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int32),
+        ("units", ctypes.c_int32),
+        ("max_splits", ctypes.c_int32),
+        ("merge_active", ctypes.c_int32),
+        ("waves_per_unit", ctypes.c_int32),
+        ("token_groups", ctypes.c_int32),
+        ("row_waves", ctypes.c_int32),
+        ("uploaded", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class BlockAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"blockattn status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+_lib = None
+
+
+def load_library():
+    """Load libblockattn.so (built in-tree by __graft_entry__.build()); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "(there is no fallback path)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
+    pp = ctypes.POINTER(blockattn_params)
+    lib.blockattn_workspace_size.argtypes = [pp, i32p, ctypes.POINTER(ctypes.c_size_t)]
+    lib.blockattn_plan.argtypes = [pp, i32p, vp, ctypes.c_size_t, vp, ctypes.POINTER(vp)]
+    fwd = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.blockattn_forward.argtypes = fwd
+    lib.blockattn_windowed_forward.argtypes = fwd
+    lib.blockattn_plan_info.argtypes = [vp, ctypes.POINTER(blockattn_plan_info_t)]
+    lib.blockattn_plan_destroy.argtypes = [vp]
+    lib.blockattn_plan_destroy.restype = None
+    lib.blockattn_last_error.restype = ctypes.c_char_p
+    for name in ("blockattn_workspace_size", "blockattn_plan", "blockattn_forward",
+                 "blockattn_windowed_forward", "blockattn_plan_info"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def blockattn_last_error() -> str:
+    return load_library().blockattn_last_error().decode()
+
+
+def _check(status: int):
+    if status != BLOCKATTN_OK:
+        raise BlockAttnError(status, blockattn_last_error())
+
+
+def make_params(*, batch, block_size, num_q_heads, num_kv_heads, head_dim, page_size, page_table_stride, num_pages,
+                sm_scale, window_left=-1, window_right=-1, splits_override=0) -> blockattn_params:
+    return blockattn_params(batch, block_size, num_q_heads, num_kv_heads, head_dim, page_size, page_table_stride,
+                            num_pages, window_left, window_right, float(sm_scale), splits_override)
+
+
+def _host_lens(seq_lens_host):
+    if hasattr(seq_lens_host, "detach"):
+        seq_lens_host = seq_lens_host.detach().cpu().numpy()
+    arr = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def blockattn_workspace_size(params: blockattn_params, seq_lens_host) -> int:
+    lib = load_library()
+    arr, p = _host_lens(seq_lens_host)
+    if arr.shape[0] < params.batch:
+        raise ValueError("seq_lens_host has fewer than batch entries")
+    out = ctypes.c_size_t(0)
+    _check(lib.blockattn_workspace_size(ctypes.byref(params), p, ctypes.byref(out)))
+    return int(out.value)
+
+
+class Plan:
+    """Owns a blockattn plan handle; remembers its params for the host-side buffer checks."""
+
+    def __init__(self, handle, params: blockattn_params, workspace):
+        self.handle = handle
+        self.params = params
+        self.workspace = workspace
+
+    def info(self) -> dict:
+        return blockattn_plan_info(self)
+
+    def destroy(self):
+        if self.handle:
+            blockattn_plan_destroy(self)
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:  # interpreter shutdown
+            pass
+
+
+def blockattn_plan(params: blockattn_params, seq_lens_host, workspace=None, workspace_bytes=None,
+                   stream=None) -> Plan:
+    """Validate and plan; with a workspace tensor, enqueue the work-list upload on the stream."""
+    lib = load_library()
+    arr, p = _host_lens(seq_lens_host)
+    if arr.shape[0] < params.batch:
+        raise ValueError("seq_lens_host has fewer than batch entries")
+    handle = ctypes.c_void_p(0)
+    if workspace is None:
+        _check(lib.blockattn_plan(ctypes.byref(params), p, None, 0, None, ctypes.byref(handle)))
+    else:
+        nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
+        if not workspace.is_cuda:
+            raise ValueError("workspace must be a device tensor")
+        _check(lib.blockattn_plan(ctypes.byref(params), p, ctypes.c_void_p(_ptr(workspace)), nbytes,
+                                  ctypes.c_void_p(_stream(stream)), ctypes.byref(handle)))
+    return Plan(handle.value, params, workspace)
+
+
+def blockattn_plan_info(plan: Plan) -> dict:
+    info = blockattn_plan_info_t()
+    _check(load_library().blockattn_plan_info(ctypes.c_void_p(plan.handle), ctypes.byref(info)))
+    return {name: getattr(info, name) for name, _ in blockattn_plan_info_t._fields_}
+
+
+def blockattn_plan_destroy(plan: Plan):
+    if plan.handle:
+        load_library().blockattn_plan_destroy(ctypes.c_void_p(plan.handle))
+        plan.handle = None
+
+
+def _expect(name, t, numel, dtypes):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if str(t.dtype).replace("torch.", "") not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}; expected one of {dtypes}")
+    if t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements; expected {numel}")
+
+
+def _check_buffers(plan: Plan, q, k_cache, v_cache, page_table, seq_lens, out, lse):
+    p = plan.params
+    rows = p.batch * p.block_size * p.num_q_heads
+    _expect("q", q, rows * p.head_dim, ("bfloat16", "int16", "uint16"))
+    _expect("out", out, rows * p.head_dim, ("bfloat16", "int16", "uint16"))
+    pool = p.num_pages * p.num_kv_heads * p.page_size * p.head_dim
+    _expect("k_cache", k_cache, pool, ("bfloat16", "int16", "uint16"))
+    _expect("v_cache", v_cache, pool, ("bfloat16", "int16", "uint16"))
+    _expect("page_table", page_table, p.batch * p.page_table_stride, ("int32",))
+    _expect("seq_lens", seq_lens, p.batch, ("int32",))
+    if lse is not None:
+        _expect("lse", lse, rows, ("float32",))
+
+
+def _forward(fn_name, plan, q, k_cache, v_cache, page_table, seq_lens, workspace, out, lse, stream):
+    _check_buffers(plan, q, k_cache, v_cache, page_table, seq_lens, out, lse)
+    fn = getattr(load_library(), fn_name)
+    vp = ctypes.c_void_p
+    _check(fn(vp(plan.handle), vp(_ptr(q)), vp(_ptr(k_cache)), vp(_ptr(v_cache)), vp(_ptr(page_table)),
+              vp(_ptr(seq_lens)), vp(_ptr(workspace)), vp(_ptr(out)), vp(_ptr(lse)), vp(_stream(stream))))
+
+
+def blockattn_forward(plan: Plan, q, k_cache, v_cache, page_table, seq_lens, workspace, out, lse=None, stream=None):
+    """Non-causal unwindowed block attention (launch only)."""
+    _forward("blockattn_forward", plan, q, k_cache, v_cache, page_table, seq_lens, workspace, out, lse, stream)
+
+
+def blockattn_windowed_forward(plan: Plan, q, k_cache, v_cache, page_table, seq_lens, workspace, out, lse,
+                               stream=None):
+    """Non-causal windowed block attention: causal windowed decode + future-key merge (launch only)."""
+    _forward("blockattn_windowed_forward", plan, q, k_cache, v_cache, page_table, seq_lens, workspace, out, lse,
+             stream)

@@ -1,0 +1,385 @@
+// Host side of blockattn: validation, the gfx950 split-KV plan, workspace layout
+// and the C ABI declared in include/blockattn.h.
+//
+// The plan replaces two host decisions of the pages' designs: the batch-size
+// gate between decode rows and context FMHA (TensorRT-LLM PR #20374,
+// Description: the row form wins at small batch because it gives multi-CTA
+// split-KV), and the split count of the paged split-KV kernel (PR #16150,
+// commits "rework flash-decoding style" and "pass the split count as a runtime
+// argument"). Here one kernel covers every batch: the plan sizes the split count
+// per request so that the partial kernel launches about two workgroups per
+// gfx950 compute unit (256 CUs), while every split keeps enough keys that its
+// fp32 partial state stays small next to the KV bytes it reads. The workspace is
+// sized exactly and checked before anything launches, the lesson of PR #21130's
+// workspace item 3 (a stats carve that outgrew its buffer).
+#include "blockattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+using namespace blockattn;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+    g_last_error = msg;
+    return code;
+}
+
+constexpr int kNumCUs = 256;
+constexpr size_t kLdsPerCU = 160 * 1024;
+constexpr int kMaxWavesPerCU = 16;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Layout {
+    size_t work = 0, pairs = 0, m = 0, l = 0, acc = 0, total = 0;
+};
+
+}  // namespace
+
+struct blockattn_plan_s {
+    blockattn_params prm{};
+    int kind = 0;
+    int g = 1, R = 1, NB = 1;
+    KernelShape shape{};
+    bool merge_active = false;
+    int units = 0, max_splits = 0;
+    std::vector<WorkItem> work;
+    std::vector<int32_t> pair_table;
+    Layout lay;
+    void* ws = nullptr;
+    bool uploaded = false;
+    void* stage = nullptr;
+    hipEvent_t copy_done = nullptr;
+};
+
+namespace {
+
+int validate(const blockattn_params* p, const int32_t* lens) {
+    if (!p) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "params is NULL");
+    if (!lens) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "seq_lens_host is NULL; pass the host copy of the lengths");
+    if (p->batch < 1) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "batch must be >= 1");
+    if (p->block_size < 1 || p->block_size > 16)
+        return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "block_size must be in [1, 16]");
+    if (p->num_kv_heads < 1 || p->num_q_heads < 1 || p->num_q_heads % p->num_kv_heads != 0)
+        return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "num_q_heads must be a positive multiple of num_kv_heads >= 1");
+    if (p->head_dim != 64 && p->head_dim != 128)
+        return fail(BLOCKATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (the gfx950 kernels are built for those)");
+    if (p->page_size != 16 && p->page_size != 32 && p->page_size != 64 && p->page_size != 128)
+        return fail(BLOCKATTN_ERR_UNSUPPORTED, "page_size must be 16, 32, 64 or 128 tokens");
+    const int g = p->num_q_heads / p->num_kv_heads;
+    const long R = (long)p->block_size * g;
+    if (R > 16L * kMaxRowBlocks)
+        return fail(BLOCKATTN_ERR_UNSUPPORTED,
+                    "block_size * (num_q_heads / num_kv_heads) must be <= 128 query rows per kv head");
+    if (p->page_table_stride < 1) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "page_table_stride must be >= 1");
+    if (p->num_pages < 1) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "num_pages must be >= 1");
+    if (!(std::isfinite(p->sm_scale) && p->sm_scale > 0.f))
+        return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "sm_scale must be finite and > 0");
+    if (p->window_left == 0 || p->window_left < -1)
+        return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "window_left must be -1 (unwindowed) or >= 1 keys");
+    if (p->window_right < -1) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "window_right must be >= -1");
+    if (p->window_left == -1 && p->window_right != -1)
+        return fail(BLOCKATTN_ERR_INVALID_ARGUMENT,
+                    "window_right must be -1 for the unwindowed form (window_left = -1)");
+    if (p->splits_override < 0) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "splits_override must be >= 0");
+    const long max_keys = (long)p->page_table_stride * p->page_size;
+    if (max_keys > (1L << 30))
+        return fail(BLOCKATTN_ERR_UNSUPPORTED, "page_table_stride * page_size must be <= 2^30 keys");
+    for (int b = 0; b < p->batch; ++b) {
+        if (lens[b] < p->block_size) {
+            char buf[160];
+            snprintf(buf, sizeof buf, "seq_lens[%d] = %d is below block_size %d: lengths count context + block keys",
+                     b, lens[b], p->block_size);
+            return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, buf);
+        }
+        if ((long)lens[b] > max_keys) {
+            char buf[160];
+            snprintf(buf, sizeof buf, "seq_lens[%d] = %d needs more than page_table_stride = %d pages of %d tokens",
+                     b, lens[b], p->page_table_stride, p->page_size);
+            return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, buf);
+        }
+    }
+    return BLOCKATTN_OK;
+}
+
+// Key tiles a request needs: 32-token tiles covering the union of its rows' key sets
+// (the causal windows for the windowed form; the future keys are merged later).
+int tiles_for(const blockattn_params* p, int n) {
+    const int c = n - p->block_size;
+    const int lo = p->window_left > 0 ? std::max(0, c - p->window_left + 1) : 0;
+    return (n + kTileTokens - 1) / kTileTokens - lo / kTileTokens;
+}
+
+KernelShape choose_shape(int D, int NB) {
+    KernelShape s{};
+    s.head_dim = D;
+    // D = 64: up to two 16-row blocks per wave, one wave per tile when R <= 32.
+    // D = 128: one row block per wave and at least two waves per tile, so no wave
+    // stages more than half of a 16 KiB tile in registers.
+    if (D == 64) {
+        s.nbw = NB <= 2 ? NB : 2;
+        s.row_waves = (NB + s.nbw - 1) / s.nbw;
+    } else {
+        s.nbw = 1;
+        s.row_waves = std::max(2, NB);
+    }
+    s.token_groups = std::max(1, std::min(4, kMaxWaves / s.row_waves));
+    const int nch = D / 8;
+    const int need = (nch + s.row_waves - 1) / s.row_waves;
+    s.cpw = need <= 4 ? 4 : (need <= 8 ? 8 : 16);
+    s.lds_bytes = partial_lds_bytes(D, s.nbw, s.row_waves, s.token_groups);
+    while (s.lds_bytes > kLdsPerCU && s.token_groups > 1) {
+        --s.token_groups;
+        s.lds_bytes = partial_lds_bytes(D, s.nbw, s.row_waves, s.token_groups);
+    }
+    return s;
+}
+
+int build_plan(const blockattn_params* p, const int32_t* lens, blockattn_plan_s* pl) {
+    int rc = validate(p, lens);
+    if (rc) return rc;
+    pl->prm = *p;
+    pl->kind = p->window_left == -1 ? 0 : 1;
+    pl->g = p->num_q_heads / p->num_kv_heads;
+    pl->R = p->block_size * pl->g;
+    pl->NB = (pl->R + 15) / 16;
+    pl->shape = choose_shape(p->head_dim, pl->NB);
+    pl->merge_active = pl->kind == 1 && p->block_size > 1 && p->window_right != 0;
+
+    const int B = p->batch, H = p->num_kv_heads;
+    std::vector<int> nt(B);
+    long total = 0;
+    for (int b = 0; b < B; ++b) {
+        nt[b] = tiles_for(p, lens[b]);
+        total += (long)nt[b] * H;
+    }
+    const int waves = pl->shape.row_waves * pl->shape.token_groups;
+    int wg_per_cu = (int)std::max<size_t>(1, kLdsPerCU / std::max<size_t>(pl->shape.lds_bytes, 1));
+    wg_per_cu = std::max(1, std::min(wg_per_cu, kMaxWavesPerCU / waves));
+    const long target_units = (long)kNumCUs * wg_per_cu;
+    // A split's partial state is R*(D+2) floats; 4*D bytes per key are streamed. Keep at
+    // least R/4 tiles per split (partial traffic <= ~1/8 of the KV bytes) and one tile per
+    // token group.
+    const long min_tiles = std::max<long>(pl->shape.token_groups, (pl->R + 3) / 4);
+    const long per_unit = std::max(min_tiles, (total + target_units - 1) / target_units);
+
+    pl->work.clear();
+    pl->pair_table.assign((size_t)B * H * 2, 0);
+    pl->max_splits = 0;
+    for (int b = 0; b < B; ++b) {
+        int S = p->splits_override > 0 ? p->splits_override : (int)((nt[b] + per_unit - 1) / per_unit);
+        S = std::max(1, std::min(S, nt[b]));
+        pl->max_splits = std::max(pl->max_splits, S);
+        for (int h = 0; h < H; ++h) {
+            const size_t pair = (size_t)b * H + h;
+            pl->pair_table[2 * pair] = (int32_t)pl->work.size();
+            pl->pair_table[2 * pair + 1] = S;
+            for (int s = 0; s < S; ++s) pl->work.push_back(WorkItem{b, h, s, S});
+        }
+    }
+    if (pl->work.size() > 0x7FFFFFFFu / 2)
+        return fail(BLOCKATTN_ERR_UNSUPPORTED, "too many work units; lower batch or splits_override");
+    pl->units = (int)pl->work.size();
+
+    Layout& L = pl->lay;
+    L.work = 0;
+    L.pairs = align_up(L.work + pl->work.size() * sizeof(WorkItem), 256);
+    L.m = align_up(L.pairs + pl->pair_table.size() * sizeof(int32_t), 256);
+    L.l = align_up(L.m + (size_t)pl->units * pl->R * sizeof(float), 256);
+    L.acc = align_up(L.l + (size_t)pl->units * pl->R * sizeof(float), 256);
+    L.total = align_up(L.acc + (size_t)pl->units * pl->R * p->head_dim * sizeof(float), 256);
+    return BLOCKATTN_OK;
+}
+
+int check_forward(blockattn_plan_t plan, int kind, const void* q, const void* k, const void* v, const int32_t* pt,
+                  const int32_t* lens, void* ws, void* out, float* lse) {
+    if (!plan) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "plan is NULL");
+    if (plan->kind != kind)
+        return fail(BLOCKATTN_ERR_PLAN_MISMATCH,
+                    kind == 0 ? "plan is windowed (window_left >= 1); call blockattn_windowed_forward"
+                              : "plan is unwindowed (window_left = -1); call blockattn_forward");
+    if (!plan->uploaded)
+        return fail(BLOCKATTN_ERR_PLAN_MISMATCH, "plan was made without a workspace; plan again with one");
+    if (ws != plan->ws)
+        return fail(BLOCKATTN_ERR_PLAN_MISMATCH, "workspace differs from the one the plan was uploaded to");
+    if (!q || !k || !v || !pt || !lens || !out)
+        return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "q, k_cache, v_cache, page_table, seq_lens and out are required");
+    if (kind == 1 && !lse)
+        return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "the windowed forward returns the merged LSE: lse is required");
+    return BLOCKATTN_OK;
+}
+
+int run_forward(blockattn_plan_t plan, const void* q, const void* k, const void* v, const int32_t* pt,
+                const int32_t* lens, void* ws, void* out, float* lse, void* stream) {
+    const blockattn_params& p = plan->prm;
+    char* base = static_cast<char*>(ws);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+
+    PartialArgs pa{};
+    pa.q = static_cast<const uint16_t*>(q);
+    pa.kc = static_cast<const uint16_t*>(k);
+    pa.vc = static_cast<const uint16_t*>(v);
+    pa.page_table = pt;
+    pa.seq_lens = lens;
+    pa.work = reinterpret_cast<const WorkItem*>(base + plan->lay.work);
+    pa.part_m = reinterpret_cast<float*>(base + plan->lay.m);
+    pa.part_l = reinterpret_cast<float*>(base + plan->lay.l);
+    pa.part_acc = reinterpret_cast<float*>(base + plan->lay.acc);
+    pa.K = p.block_size;
+    pa.Hq = p.num_q_heads;
+    pa.Hkv = p.num_kv_heads;
+    pa.g = plan->g;
+    pa.R = plan->R;
+    pa.P = p.page_size;
+    pa.stride = p.page_table_stride;
+    pa.num_pages = p.num_pages;
+    pa.window_left = p.window_left;
+    pa.row_waves = plan->shape.row_waves;
+    pa.token_groups = plan->shape.token_groups;
+    pa.scale_log2 = (float)((double)p.sm_scale * 1.4426950408889634);
+    hipError_t e = launch_partial(plan->shape, plan->kind == 1, plan->units, pa, st);
+    if (e != hipSuccess) return fail(BLOCKATTN_ERR_HIP, std::string("partial kernel launch: ") + hipGetErrorString(e));
+
+    CombineArgs ca{};
+    ca.q = pa.q;
+    ca.kc = pa.kc;
+    ca.vc = pa.vc;
+    ca.page_table = pt;
+    ca.seq_lens = lens;
+    ca.pair_table = reinterpret_cast<const int32_t*>(base + plan->lay.pairs);
+    ca.part_m = pa.part_m;
+    ca.part_l = pa.part_l;
+    ca.part_acc = pa.part_acc;
+    ca.out = static_cast<uint16_t*>(out);
+    ca.lse = lse;
+    ca.K = p.block_size;
+    ca.Hq = p.num_q_heads;
+    ca.Hkv = p.num_kv_heads;
+    ca.g = plan->g;
+    ca.R = plan->R;
+    ca.P = p.page_size;
+    ca.stride = p.page_table_stride;
+    ca.num_pages = p.num_pages;
+    ca.window_right = p.window_right;
+    ca.scale_log2 = pa.scale_log2;
+    const int rows = p.batch * p.num_kv_heads * plan->R;
+    e = launch_combine(p.head_dim, plan->merge_active, rows, ca, st);
+    if (e != hipSuccess) return fail(BLOCKATTN_ERR_HIP, std::string("combine kernel launch: ") + hipGetErrorString(e));
+    return BLOCKATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int blockattn_workspace_size(const blockattn_params* params, const int32_t* seq_lens_host, size_t* bytes) {
+    if (!bytes) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    blockattn_plan_s tmp;
+    int rc = build_plan(params, seq_lens_host, &tmp);
+    if (rc) return rc;
+    *bytes = tmp.lay.total;
+    g_last_error.clear();
+    return BLOCKATTN_OK;
+}
+
+int blockattn_plan(const blockattn_params* params, const int32_t* seq_lens_host, void* workspace,
+                   size_t workspace_bytes, void* stream, blockattn_plan_t* plan) {
+    if (!plan) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "plan is NULL");
+    *plan = nullptr;
+    blockattn_plan_s* pl = new (std::nothrow) blockattn_plan_s();
+    if (!pl) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "out of host memory");
+    int rc = build_plan(params, seq_lens_host, pl);
+    if (rc) {
+        delete pl;
+        return rc;
+    }
+    if (workspace) {
+        if (workspace_bytes < pl->lay.total) {
+            char buf[200];
+            snprintf(buf, sizeof buf, "workspace has %zu bytes but this plan needs %zu (blockattn_workspace_size)",
+                     workspace_bytes, pl->lay.total);
+            delete pl;
+            return fail(BLOCKATTN_ERR_WORKSPACE_TOO_SMALL, buf);
+        }
+        const size_t head = pl->lay.m;  // work list + pair table
+        hipError_t e = hipHostMalloc(&pl->stage, head, hipHostMallocDefault);
+        if (e != hipSuccess) {
+            delete pl;
+            return fail(BLOCKATTN_ERR_HIP, std::string("hipHostMalloc: ") + hipGetErrorString(e));
+        }
+        std::memset(pl->stage, 0, head);
+        std::memcpy(static_cast<char*>(pl->stage) + pl->lay.work, pl->work.data(), pl->work.size() * sizeof(WorkItem));
+        std::memcpy(static_cast<char*>(pl->stage) + pl->lay.pairs, pl->pair_table.data(),
+                    pl->pair_table.size() * sizeof(int32_t));
+        hipStream_t st = static_cast<hipStream_t>(stream);
+        e = hipMemcpyAsync(workspace, pl->stage, head, hipMemcpyHostToDevice, st);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&pl->copy_done, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventRecord(pl->copy_done, st);
+        if (e != hipSuccess) {
+            blockattn_plan_destroy(pl);
+            return fail(BLOCKATTN_ERR_HIP, std::string("work-list upload: ") + hipGetErrorString(e));
+        }
+        pl->ws = workspace;
+        pl->uploaded = true;
+    }
+    *plan = pl;
+    g_last_error.clear();
+    return BLOCKATTN_OK;
+}
+
+int blockattn_forward(blockattn_plan_t plan, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* page_table, const int32_t* seq_lens, void* workspace, void* out, float* lse,
+                      void* stream) {
+    int rc = check_forward(plan, 0, q, k_cache, v_cache, page_table, seq_lens, workspace, out, lse);
+    if (rc) return rc;
+    return run_forward(plan, q, k_cache, v_cache, page_table, seq_lens, workspace, out, lse, stream);
+}
+
+int blockattn_windowed_forward(blockattn_plan_t plan, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* page_table, const int32_t* seq_lens, void* workspace, void* out,
+                               float* lse, void* stream) {
+    int rc = check_forward(plan, 1, q, k_cache, v_cache, page_table, seq_lens, workspace, out, lse);
+    if (rc) return rc;
+    return run_forward(plan, q, k_cache, v_cache, page_table, seq_lens, workspace, out, lse, stream);
+}
+
+int blockattn_plan_info(blockattn_plan_t plan, blockattn_plan_info_t* info) {
+    if (!plan || !info) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "plan and info are required");
+    info->kind = plan->kind;
+    info->units = plan->units;
+    info->max_splits = plan->max_splits;
+    info->merge_active = plan->merge_active ? 1 : 0;
+    info->waves_per_unit = plan->shape.row_waves * plan->shape.token_groups;
+    info->token_groups = plan->shape.token_groups;
+    info->row_waves = plan->shape.row_waves;
+    info->uploaded = plan->uploaded ? 1 : 0;
+    info->workspace_bytes = plan->lay.total;
+    return BLOCKATTN_OK;
+}
+
+void blockattn_plan_destroy(blockattn_plan_t plan) {
+    if (!plan) return;
+    if (plan->copy_done) {
+        (void)hipEventSynchronize(plan->copy_done);
+        (void)hipEventDestroy(plan->copy_done);
+    }
+    if (plan->stage) (void)hipHostFree(plan->stage);
+    delete plan;
+}
+
+const char* blockattn_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+"""The C-ABI library on the host: exported symbols, validation, planning and sizing (no GPU)."""
+import ctypes
+import re
+import os
+
+import numpy as np
+import pytest
+
+import speculative_decoding_draft_paged_amd as ba
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "blockattn.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|void|const char\*)\s+(blockattn_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ba.load_library()
+    names = header_functions()
+    assert set(names) == set(ba.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_layouts_match_header():
+    # params: 11 int32 + 1 float = 48 bytes; info: 8 int32 + size_t
+    assert ctypes.sizeof(ba.blockattn_params) == 48
+    assert ctypes.sizeof(ba.blockattn_plan_info_t) == 40
+
+
+def params(**kw):
+    base = dict(batch=2, block_size=7, num_q_heads=8, num_kv_heads=2, head_dim=64, page_size=32,
+                page_table_stride=4200, num_pages=9000, sm_scale=0.125)
+    base.update(kw)
+    return ba.make_params(**base)
+
+
+def plan_info(prm, lens):
+    plan = ba.blockattn_plan(prm, lens)
+    info = plan.info()
+    plan.destroy()
+    return info
+
+
+def test_host_only_plan_and_info():
+    info = plan_info(params(), [131079, 131079])
+    assert info["kind"] == 0 and info["uploaded"] == 0 and info["merge_active"] == 0
+    assert info["units"] >= 256 and info["max_splits"] >= 64
+    assert info["workspace_bytes"] == ba.blockattn_workspace_size(params(), [131079, 131079])
+
+
+def test_split_heuristic_fills_the_gpu_and_bounds_partials():
+    # one request, 128K keys, 2 kv heads: many splits; 32 requests x 16 heads: one split each
+    small = plan_info(params(batch=1), [131079])
+    assert small["units"] >= 256
+    big = plan_info(params(batch=32, num_q_heads=64, num_kv_heads=16), [131079] * 32)
+    assert big["max_splits"] == 1 and big["units"] == 512
+    # every split keeps >= R/4 tiles of keys
+    tiny = plan_info(params(batch=1), [200])
+    assert tiny["max_splits"] == 1
+
+
+def test_splits_override_and_clamp():
+    info = plan_info(params(batch=1, splits_override=5), [1000])
+    assert info["max_splits"] == 5 and info["units"] == 10
+    info = plan_info(params(batch=1, splits_override=10 ** 6), [1000])
+    assert info["max_splits"] == (1000 + 31) // 32
+
+
+def test_windowed_plan_merge_flag():
+    w = dict(head_dim=128, page_size=64, num_q_heads=16, num_kv_heads=1, window_left=4096)
+    assert plan_info(params(**w, block_size=7, window_right=-1), [8199, 8199])["merge_active"] == 1
+    assert plan_info(params(**w, block_size=1, window_right=-1), [8193, 8193])["merge_active"] == 0
+    assert plan_info(params(**w, block_size=7, window_right=0), [8199, 8199])["merge_active"] == 0
+    info = plan_info(params(**w, block_size=7, window_right=-1), [8199, 8199])
+    assert info["kind"] == 1 and info["row_waves"] == 7
+
+
+@pytest.mark.parametrize("B", [1, 2, 32, 33, 200])
+def test_workspace_size_grows_with_batch(B):
+    lens = np.full(B, 32775, np.int32)
+    nbytes = ba.blockattn_workspace_size(params(batch=B, page_table_stride=1100), lens)
+    info = plan_info(params(batch=B, page_table_stride=1100), lens)
+    R, D = 28, 64
+    floats = info["units"] * R * (D + 2) * 4
+    assert floats <= nbytes <= floats + info["units"] * 16 + B * 2 * 8 + 4 * 256
+
+
+@pytest.mark.parametrize("kw,lens,code,needle", [
+    (dict(head_dim=96), [100, 100], ba.BLOCKATTN_ERR_UNSUPPORTED, "head_dim"),
+    (dict(page_size=48), [100, 100], ba.BLOCKATTN_ERR_UNSUPPORTED, "page_size"),
+    (dict(num_q_heads=7), [100, 100], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "num_q_heads"),
+    (dict(block_size=17), [100, 100], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "block_size"),
+    (dict(num_q_heads=40, num_kv_heads=1, block_size=4), [100, 100], ba.BLOCKATTN_ERR_UNSUPPORTED, "128"),
+    (dict(), [6, 100], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "seq_lens[0]"),
+    (dict(page_table_stride=3), [100, 97], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "page_table_stride"),
+    (dict(window_left=0), [100, 100], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "window_left"),
+    (dict(window_right=3), [100, 100], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "window_right"),
+    (dict(sm_scale=float("nan")), [100, 100], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "sm_scale"),
+])
+def test_invalid_parameters_are_named(kw, lens, code, needle):
+    with pytest.raises(ba.BlockAttnError) as e:
+        ba.blockattn_plan(params(**kw), lens)
+    assert e.value.status == code
+    assert needle in e.value.message
+
+
+def test_forward_refuses_plans_without_workspace_or_wrong_kind():
+    lib = ba.load_library()
+    plan = ba.blockattn_plan(params(), [100, 100])
+    vp = ctypes.c_void_p
+    one = vp(0x1000)
+    rc = lib.blockattn_forward(vp(plan.handle), one, one, one, one, one, one, one, None, None)
+    assert rc == ba.BLOCKATTN_ERR_PLAN_MISMATCH and "workspace" in ba.blockattn_last_error()
+    rc = lib.blockattn_windowed_forward(vp(plan.handle), one, one, one, one, one, one, one, one, None)
+    assert rc == ba.BLOCKATTN_ERR_PLAN_MISMATCH and "blockattn_forward" in ba.blockattn_last_error()
+    plan.destroy()

@@ -1,0 +1,157 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI (MI355X only).
+
+Small cases are compared element by element over every row; they span several
+32-token tiles, ragged page tails, empty contexts, odd row counts and forced
+split counts. The pools' unused slots and the extra fill page hold bf16 NaN,
+so a stale-slot leak shows up as a non-finite output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth.configs import Case
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+def case(idx, *, batch=2, K=3, hq=4, hkv=1, D=64, P=32, ctx=100, ctx_range=None, wl=-1, wr=-1, outliers=0.0):
+    return Case(f"g{idx}", 80, idx, batch=batch, block_size=K, num_q_heads=hq, num_kv_heads=hkv, head_dim=D,
+                page_size=P, context=ctx, context_range=ctx_range, window_left=wl, window_right=wr,
+                outlier_rate=outliers)
+
+
+def check_full(c, label, **run_kw):
+    inp = synth.make_inputs(c)
+    dc = H.upload(inp)
+    out, lse, info = H.run(dc, **run_kw)
+    wl = run_kw.get("window_left", c.window_left)
+    wr = run_kw.get("window_right", c.window_right)
+    ref_out, ref_lse = oracle.attention_case(inp, window_left=wl, window_right=wr)
+    res = H.compare(out, lse, ref_out, ref_lse, label=label)
+    print(f"{label}: {res} info={info}", flush=True)
+    return out, lse, info
+
+
+def test_cfg1_tiny():
+    c = synth.cases_for_config(1)[0]
+    check_full(c, "cfg1")
+
+
+SMALL = [
+    # (idx, kwargs)
+    (1, dict(batch=1, K=3, hq=4, hkv=1, D=64, P=32, ctx=0)),          # empty context: only block keys
+    (2, dict(batch=2, K=7, hq=8, hkv=2, D=64, P=32, ctx=1000)),       # R = 28, ragged tail
+    (3, dict(batch=3, K=3, hq=6, hkv=3, D=64, P=16, ctx_range=(40, 300))),  # R = 6, P = 16, mixed lengths
+    (4, dict(batch=2, K=4, hq=10, hkv=2, D=64, P=64, ctx=513)),       # group 5, R = 20
+    (5, dict(batch=1, K=7, hq=16, hkv=1, D=64, P=32, ctx=777)),       # R = 112 on D = 64
+    (6, dict(batch=2, K=1, hq=16, hkv=1, D=128, P=64, ctx=300)),      # R = 16, D = 128
+    (7, dict(batch=2, K=3, hq=16, hkv=1, D=128, P=64, ctx=2100)),     # R = 48
+    (8, dict(batch=2, K=7, hq=16, hkv=1, D=128, P=128, ctx=950)),     # R = 112, P = 128
+    (9, dict(batch=2, K=7, hq=8, hkv=2, D=64, P=32, ctx=4096)),       # page-aligned end
+]
+
+
+@pytest.mark.parametrize("idx,kw", SMALL, ids=[f"s{i}" for i, _ in SMALL])
+def test_unwindowed_small(idx, kw):
+    check_full(case(idx, **kw), f"unwindowed s{idx}")
+
+
+WSMALL = [
+    (21, dict(batch=2, K=7, hq=16, hkv=1, D=128, P=64, ctx=3000, wl=256, wr=-1)),
+    (22, dict(batch=3, K=3, hq=64, hkv=4, D=128, P=64, ctx_range=(100, 1500), wl=300, wr=-1, outliers=0.01)),
+    (23, dict(batch=2, K=7, hq=8, hkv=2, D=64, P=32, ctx=500, wl=33, wr=2)),
+    (24, dict(batch=2, K=3, hq=16, hkv=1, D=128, P=64, ctx=10, wl=4096, wr=-1)),  # window longer than cache
+    (25, dict(batch=2, K=7, hq=16, hkv=1, D=128, P=64, ctx=700, wl=1, wr=-1)),    # self + later keys only
+]
+
+
+@pytest.mark.parametrize("idx,kw", WSMALL, ids=[f"w{i}" for i, _ in WSMALL])
+def test_windowed_small(idx, kw):
+    _, _, info = check_full(case(idx, **kw), f"windowed w{idx}")
+    assert info["merge_active"] == 1
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 1000])
+def test_split_invariance(splits):
+    c = case(30, batch=2, K=7, hq=8, hkv=2, D=64, P=32, ctx=3000)
+    inp = synth.make_inputs(c)
+    dc = H.upload(inp)
+    ref_out, ref_lse = oracle.attention_case(inp)
+    out, lse, info = H.run(dc, splits=splits)
+    H.compare(out, lse, ref_out, ref_lse, label=f"splits={splits}")
+    assert info["max_splits"] == min(splits, (3000 + 7 + 31) // 32)
+    base, base_lse, _ = H.run(dc, splits=1)
+    # different split counts only reorder fp32 sums: agreement well inside the parity bar
+    assert np.abs(out - base).max() <= 4 * H.ulp_bf16(float(np.abs(base).max()))
+
+
+def test_empty_splits_from_shorter_live_lengths():
+    """Plan with long host lengths, run with shorter device lengths: trailing splits get no tiles."""
+    c = case(31, batch=2, K=3, hq=4, hkv=1, D=64, P=32, ctx=2000)
+    inp = synth.make_inputs(c)
+    dc = H.upload(inp)
+    short = inp.seq_lens.copy()
+    short[:] = [500, 37]
+    dc.seq_lens = torch.from_numpy(short).cuda()
+    out, lse, info = H.run(dc, plan_lens=inp.seq_lens, splits=16)
+    inp2 = synth.Inputs(c, inp.q, inp.k_pool, inp.v_pool, inp.page_table, short)
+    ref_out, ref_lse = oracle.attention_case(inp2)
+    H.compare(out, lse, ref_out, ref_lse, label="empty splits")
+
+
+def test_windowed_full_window_equals_unwindowed():
+    c = case(32, batch=2, K=7, hq=16, hkv=1, D=128, P=64, ctx=2048, wl=4096, wr=-1)
+    inp = synth.make_inputs(c)
+    dc = H.upload(inp)
+    w_out, w_lse, _ = H.run(dc)
+    u_out, u_lse, _ = H.run(dc, window_left=-1, window_right=-1)
+    ref_out, ref_lse = oracle.attention_case(inp)
+    H.compare(w_out, w_lse, ref_out, ref_lse, label="windowed W>=N")
+    H.compare(u_out, u_lse, ref_out, ref_lse, label="unwindowed")
+    assert np.abs(w_out - u_out).max() <= 2 * H.ulp_bf16(float(np.abs(u_out).max()))
+
+
+def test_block_of_one_skips_merge_bit_identical():
+    c = case(33, batch=3, K=1, hq=16, hkv=1, D=128, P=64, ctx=5000, wl=4096, wr=-1)
+    inp = synth.make_inputs(c)
+    dc = H.upload(inp)
+    out_a, lse_a, info_a = H.run(dc)
+    out_b, lse_b, info_b = H.run(dc, window_right=0)
+    assert info_a["merge_active"] == 0 and info_b["merge_active"] == 0
+    np.testing.assert_array_equal(out_a, out_b)
+    np.testing.assert_array_equal(lse_a, lse_b)
+    ref_out, ref_lse = oracle.attention_case(inp)
+    H.compare(out_a, lse_a, ref_out, ref_lse, label="K=1 windowed")
+
+
+def test_page_permutation_and_batch_independence():
+    c = case(34, batch=3, K=7, hq=8, hkv=2, D=64, P=32, ctx_range=(200, 900))
+    inp = synth.make_inputs(c)
+    base, base_lse, _ = H.run(H.upload(inp))
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(inp.num_pages)
+    inv = np.argsort(perm)
+    moved = synth.Inputs(c, inp.q, inp.k_pool[perm].copy(), inp.v_pool[perm].copy(),
+                         inv[inp.page_table].astype(np.int32), inp.seq_lens)
+    out, lse, _ = H.run(H.upload(moved))
+    np.testing.assert_array_equal(out, base)
+    np.testing.assert_array_equal(lse, base_lse)
+    one = Case("g34b", 80, 34, batch=1, block_size=7, num_q_heads=8, num_kv_heads=2, head_dim=64, page_size=32,
+               context=int(inp.seq_lens[1]) - 7)
+    single = synth.Inputs(one, inp.q[1:2].copy(), inp.k_pool, inp.v_pool, inp.page_table[1:2].copy(),
+                          inp.seq_lens[1:2].copy())
+    out1, lse1, _ = H.run(H.upload(single))
+    ref_out, ref_lse = oracle.attention_case(single)
+    H.compare(out1, lse1, ref_out, ref_lse, label="request alone")
+    H.compare(base[1:2], base_lse[1:2], ref_out, ref_lse, label="request in batch")
+
+
+def test_workspace_canary_and_no_nan_leak():
+    c = case(35, batch=2, K=7, hq=8, hkv=2, D=64, P=32, ctx=1234)
+    inp = synth.make_inputs(c)
+    assert (inp.k_pool[-1] == synth.BF16_NAN).all()
+    out, lse, _ = H.run(H.upload(inp), canary=True)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
