@@ -1,0 +1,358 @@
+#!/usr/bin/env python3
+"""Benchmark of draft-block paged attention on one MI355X.
+
+Workload (default): the Kimi-style TP8 rank of a 64q/16kv GQA drafter, i.e.
+8 q / 2 kv heads, head_dim 64, block K = 7, 128K-token contexts, page 32, HND
+bf16 pools, B = 8 requests with disjoint shuffled page ranges; synthetic N(0,1)
+data from the seeded generator. One step = one blockattn_forward call for the
+whole batch (plan once, outside timing): the split-KV partial kernel and the
+LSE combine.
+
+Timing: the K timed steps are one captured HIP graph, replayed between two
+device synchronisations; each step reads the next of M copies of the K/V pools
+(M * pool >= 1 GiB) so the 256 MB Infinity Cache cannot serve repeats. HIP
+events recorded around every partial-kernel launch give that kernel's average
+duration (a separate pass of K eager calls), from which the roofline fraction is computed.
+
+Output: one JSON line (metric, value in GB/s of algorithmic KV bytes, ...,
+roofline, cpu_baseline). The cpu_baseline leg times the fp64 oracle on a
+bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "us per block-attention call and achieved HBM GB/s (KV read) vs MI355X peak"
+# Pages' number for this workload (TensorRT-LLM PR #20374, B > 1 comment): 8q/2kv heads, D 64,
+# page 32, K 7, 128K context, B = 8, decode-row form: 252.4 us per attention op on SM107.
+# Unique KV bytes / time = 536.9 MB / 252.4 us = 2127 GB/s. Another machine: context only.
+PAGES_CONTEXT = {"cfg2_b8_128k": 536_895_488 / 252.4e-6 / 1e9, "cfg2_b16_128k": 1_073_790_976 / 492.9e-6 / 1e9,
+                 "cfg2_b8_32k": 134_246_400 / 65.7e-6 / 1e9, "cfg2_b16_32k": 268_492_800 / 131.3e-6 / 1e9}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kv_bytes(case, seq_lens) -> int:
+    """Algorithmic KV bytes of one call: every key a row needs, read once (K and V, 2 B each)."""
+    total = 0
+    for n in seq_lens.tolist():
+        c = n - case.block_size
+        lo = max(0, c - case.window_left + 1) if case.window_left > 0 else 0
+        total += case.num_kv_heads * (n - lo) * 4 * case.head_dim
+    return total
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch loaded (shared with the library)."""
+
+    def __init__(self):
+        import torch
+
+        lib_dir = os.path.join(os.path.dirname(torch.__file__), "lib")
+        path = os.path.join(lib_dir, "libamdhip64.so")
+        self.hip = ctypes.CDLL(path if os.path.exists(path) else "libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            evs.append(e.value)
+        return evs
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for name in ("kernels.hip", "api.cpp", "internal.h"):
+        with open(os.path.join(ROOT, "speculative_decoding_draft_paged_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(case_name: str, per_launch_bytes: int):
+    """HBM bytes per launch from a committed rocprofv3 PMC summary, if it matches the current kernels."""
+    path = os.path.join(ROOT, "profiles", f"pmc_partial_{case_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_digest") != kernel_source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def run_case(case, steps, warmup, threads, graph=True):
+    import numpy as np
+    import torch
+
+    import speculative_decoding_draft_paged_amd as ba
+    import synth
+
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    inp = synth.make_inputs(case, threads=threads)
+    log(f"[bench] {case.name}: inputs generated in {time.perf_counter() - t0:.1f}s "
+        f"(pool {inp.k_pool.nbytes / 2**20:.0f} MiB per tensor)")
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q = bf(inp.q)
+    k0, v0 = bf(inp.k_pool), bf(inp.v_pool)
+    pt = torch.from_numpy(inp.page_table).to(dev)
+    lens = torch.from_numpy(inp.seq_lens).to(dev)
+    pool_bytes = 2 * inp.k_pool.nbytes
+    copies = max(1, math.ceil((1 << 30) / pool_bytes))
+    ks, vs = [k0], [v0]
+    for _ in range(copies - 1):
+        ks.append(k0.clone())
+        vs.append(v0.clone())
+    prm = ba.make_params(batch=case.batch, block_size=case.block_size, num_q_heads=case.num_q_heads,
+                         num_kv_heads=case.num_kv_heads, head_dim=case.head_dim, page_size=case.page_size,
+                         page_table_stride=inp.page_table.shape[1], num_pages=inp.num_pages, sm_scale=case.scale,
+                         window_left=case.window_left, window_right=case.window_right)
+    nbytes = ba.blockattn_workspace_size(prm, inp.seq_lens)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    plan = ba.blockattn_plan(prm, inp.seq_lens, ws, nbytes)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    fwd = ba.blockattn_windowed_forward if case.windowed else ba.blockattn_forward
+
+    def step(i):
+        fwd(plan, q, ks[i % copies], vs[i % copies], pt, lens, ws, out, lse)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ref_out = out.clone()
+
+    hip = HipEvents()
+    ga, gb = hip.create(2)
+    stream = torch.cuda.current_stream()
+    used_graph = False
+    if graph:
+        try:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(steps):
+                    step(i)
+            g.replay()  # untimed: warms the graph; its result must equal the eager result
+            torch.cuda.synchronize()
+            if not torch.equal(out, ref_out):
+                raise RuntimeError("graph replay output differs from the eager output")
+            used_graph = True
+        except Exception as e:
+            log(f"[bench] graph capture unavailable ({e}); timing eager launches")
+            torch.cuda.synchronize()
+
+    # Timed region: exactly `steps` forward calls between two device synchronisations.
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    hip.hip.hipEventRecord(ctypes.c_void_p(ga), ctypes.c_void_p(stream.cuda_stream))
+    if used_graph:
+        g.replay()
+    else:
+        for i in range(steps):
+            step(i)
+    hip.hip.hipEventRecord(ctypes.c_void_p(gb), ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    if not torch.equal(out, ref_out):
+        raise RuntimeError("timed run output differs from the warm-up output")
+    total_ms = hip.elapsed_ms(ga, gb)
+
+    # Kernel timing: HIP events recorded by the library right around every partial-kernel
+    # launch, on the stream it launches on, over `steps` eager calls.
+    before, after = hip.create(steps), hip.create(steps)
+    for i in range(steps):
+        ba.blockattn_plan_set_profile_events(plan, before[i], after[i])
+        step(i)
+    ba.blockattn_plan_set_profile_events(plan, None, None)
+    torch.cuda.synchronize()
+    kern_ms = [hip.elapsed_ms(before[i], after[i]) for i in range(steps)]
+    timing = "eager"
+    hip.destroy(before + after + [ga, gb])
+    info = plan.info()
+    res = {
+        "case": case.name,
+        "kv_bytes": kv_bytes(case, inp.seq_lens),
+        "step_ms": total_ms / steps,
+        "wall_ms": wall * 1e3 / steps,
+        "partial_ms": sum(kern_ms) / len(kern_ms),
+        "partial_ms_min": min(kern_ms),
+        "graph": used_graph,
+        "kernel_timing": timing,
+        "copies": copies,
+        "units": info["units"],
+        "max_splits": info["max_splits"],
+        "waves_per_unit": info["waves_per_unit"],
+    }
+    plan.destroy()
+    return res, inp, out
+
+
+def cpu_baseline(case, inp, gpu_out, kv_total, budget_s):
+    """Time the fp64 oracle on a bounded sample of (request, kv head) pairs of the same call."""
+    import numpy as np
+
+    import oracle
+
+    threads = oracle.default_threads()
+    pairs_all = [(b, h) for b in range(case.batch) for h in range(case.num_kv_heads)]
+    t0 = time.perf_counter()
+    out, lse = oracle.attention_case(inp, pairs=pairs_all[:1], threads=threads)
+    t1 = time.perf_counter() - t0
+    n = max(1, min(len(pairs_all), int(budget_s / max(t1, 1e-3))))
+    sample = pairs_all[:n]
+    if n > 1:
+        t0 = time.perf_counter()
+        out, lse = oracle.attention_case(inp, pairs=sample, threads=threads)
+        t1 = time.perf_counter() - t0
+    per_pair = t1 / len(sample)
+    full_s = per_pair * len(pairs_all)
+    g = case.group
+    sel = np.zeros(out.shape[:3], dtype=bool)
+    for b, h in sample:
+        sel[b, :, h * g:(h + 1) * g] = True
+    got = gpu_out.float().cpu().numpy().astype(np.float64)
+    diff = got[sel] - out[sel]
+    amax = float(np.abs(out[sel]).max())
+    ulp = 2.0 ** (math.floor(math.log2(amax)) - 7)
+    return {
+        "value": kv_total / full_s / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{len(sample)} of {len(pairs_all)} (request, kv head) pairs of the same call, "
+                  f"{t1:.1f} s fp64, scaled to the whole call ({full_s * 1e6:.0f} us per call)",
+        "us_per_call": full_s * 1e6,
+        "sample_parity": {"rel_l2": float(np.linalg.norm(diff) / np.linalg.norm(out[sel])),
+                          "max_ulp": float(np.abs(diff).max() / ulp)},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--case", default="cfg2_b8_128k", help="workload case name (see synth/configs.py)")
+    ap.add_argument("--sweep", action="store_true", help="also time every case of the same config (stderr)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU budget of the oracle sample")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device copy 5 times (reference kernel for PMC byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU; the path shards by request or kv head "
+                                   "with no exchange, so no multi-GPU figure is measured", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    from synth.configs import cases_for_config, find_case
+
+    threads = min(16, len(os.sched_getaffinity(0)))
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 5 x 1 GiB device copies done")
+
+    case = find_case(args.case)
+    res, inp, out = run_case(case, args.steps, args.warmup, threads, graph=not args.eager)
+    kvb = res["kv_bytes"]
+    value = kvb / (res["step_ms"] * 1e-3) / 1e9
+    achieved = kvb / (res["partial_ms"] * 1e-3) / 1e9
+    log(f"[bench] {case.name}: step {res['step_ms'] * 1e3:.1f} us, partial kernel {res['partial_ms'] * 1e3:.1f} us "
+        f"(min {res['partial_ms_min'] * 1e3:.1f}), {value:.0f} GB/s per step, {achieved:.0f} GB/s in the partial "
+        f"kernel, units {res['units']}, splits {res['max_splits']}, graph {res['graph']}")
+
+    sweep = None
+    if args.sweep:
+        sweep = []
+        for c in cases_for_config(case.cfg):
+            r, _, _ = run_case(c, max(10, args.steps // 2), 3, threads, graph=not args.eager)
+            r["gbs"] = r["kv_bytes"] / (r["step_ms"] * 1e-3) / 1e9
+            r["frac"] = r["gbs"] / HBM_PEAK_GBS
+            r["partial_gbs"] = r["kv_bytes"] / (r["partial_ms"] * 1e-3) / 1e9
+            sweep.append(r)
+            log(f"[sweep] {c.name:16s} {r['step_ms'] * 1e3:9.1f} us  {r['gbs']:7.0f} GB/s  "
+                f"({100 * r['frac']:5.1f} % of 8 TB/s)  partial {r['partial_ms'] * 1e3:9.1f} us "
+                f"{r['partial_gbs']:7.0f} GB/s  units {r['units']}")
+            torch.cuda.empty_cache()
+
+    traffic = load_traffic(case.name, kvb)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "us_per_call": round(res["step_ms"] * 1e3, 2),
+        "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": (round(value / PAGES_CONTEXT[case.name], 3) if case.name in PAGES_CONTEXT else None),
+        "vs_baseline_note": "ratio to the pages' SM107 decode-row figure for the same shape (another GPU: context)"
+                            if case.name in PAGES_CONTEXT else None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{case.name}: draft-block attention, {case.num_q_heads}q/{case.num_kv_heads}kv heads, "
+                               f"head_dim {case.head_dim}, K={case.block_size}, page {case.page_size}, "
+                               f"{'windowed W=%d' % case.window_left if case.windowed else 'unwindowed'}",
+                   "batch": case.batch, "context": case.context, "kv_bytes_per_call": kvb,
+                   "pool_copies_rotated": res["copies"], "hip_graph": res["graph"], "units": res["units"],
+                   "max_splits": res["max_splits"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "partial_kernel (split-KV partial attention)",
+                     "kernel_us": round(res["partial_ms"] * 1e3, 2), "kernel_events": res["kernel_timing"]},
+        "cpu_baseline": None,
+    }
+    if sweep is not None:
+        line["sweep"] = [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()} for r in sweep]
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(case, inp, out, kvb, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

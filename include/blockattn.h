@@ -144,6 +144,14 @@ int blockattn_windowed_forward(blockattn_plan_t plan, const void* q, const void*
 /* Describe the plan (path taken, units, splits, merge on or off). */
 int blockattn_plan_info(blockattn_plan_t plan, blockattn_plan_info_t* info);
 
+/*
+ * Profiling aid. When before/after are non-NULL hipEvent_t handles, every later
+ * forward on this plan records `before` on its stream right before the split-KV
+ * partial kernel and `after` right after it, so a caller can time that kernel
+ * alone with hipEventElapsedTime. Pass NULL, NULL to stop. Adds no device work.
+ */
+int blockattn_plan_set_profile_events(blockattn_plan_t plan, void* before, void* after);
+
 /* Wait for the plan's pending work-list copy, then free it. NULL is ignored. */
 void blockattn_plan_destroy(blockattn_plan_t plan);
 

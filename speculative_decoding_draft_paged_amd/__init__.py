@@ -33,6 +33,7 @@ EXPORTED = (
     "blockattn_forward",
     "blockattn_windowed_forward",
     "blockattn_plan_info",
+    "blockattn_plan_set_profile_events",
     "blockattn_plan_destroy",
     "blockattn_last_error",
 )
@@ -87,6 +88,10 @@ def load_library():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
                            "(there is no fallback path)")
+    # Load torch's HIP runtime first so the library binds to the same runtime instance
+    # (same soname): streams, events and device pointers are then shared.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
     pp = ctypes.POINTER(blockattn_params)
@@ -96,11 +101,12 @@ def load_library():
     lib.blockattn_forward.argtypes = fwd
     lib.blockattn_windowed_forward.argtypes = fwd
     lib.blockattn_plan_info.argtypes = [vp, ctypes.POINTER(blockattn_plan_info_t)]
+    lib.blockattn_plan_set_profile_events.argtypes = [vp, vp, vp]
     lib.blockattn_plan_destroy.argtypes = [vp]
     lib.blockattn_plan_destroy.restype = None
     lib.blockattn_last_error.restype = ctypes.c_char_p
     for name in ("blockattn_workspace_size", "blockattn_plan", "blockattn_forward",
-                 "blockattn_windowed_forward", "blockattn_plan_info"):
+                 "blockattn_windowed_forward", "blockattn_plan_info", "blockattn_plan_set_profile_events"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -201,6 +207,12 @@ def blockattn_plan_info(plan: Plan) -> dict:
     info = blockattn_plan_info_t()
     _check(load_library().blockattn_plan_info(ctypes.c_void_p(plan.handle), ctypes.byref(info)))
     return {name: getattr(info, name) for name, _ in blockattn_plan_info_t._fields_}
+
+
+def blockattn_plan_set_profile_events(plan: Plan, before, after):
+    """Record raw hipEvent_t handles (ints) around the partial kernel of later forwards; None stops."""
+    _check(load_library().blockattn_plan_set_profile_events(ctypes.c_void_p(plan.handle), ctypes.c_void_p(before),
+                                                            ctypes.c_void_p(after)))
 
 
 def blockattn_plan_destroy(plan: Plan):

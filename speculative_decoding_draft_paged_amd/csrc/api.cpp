@@ -63,6 +63,7 @@ struct blockattn_plan_s {
     bool uploaded = false;
     void* stage = nullptr;
     hipEvent_t copy_done = nullptr;
+    hipEvent_t prof_before = nullptr, prof_after = nullptr;
 };
 
 namespace {
@@ -250,7 +251,10 @@ int run_forward(blockattn_plan_t plan, const void* q, const void* k, const void*
     pa.row_waves = plan->shape.row_waves;
     pa.token_groups = plan->shape.token_groups;
     pa.scale_log2 = (float)((double)p.sm_scale * 1.4426950408889634);
-    hipError_t e = launch_partial(plan->shape, plan->kind == 1, plan->units, pa, st);
+    hipError_t e = hipSuccess;
+    if (plan->prof_before) e = hipEventRecord(plan->prof_before, st);
+    if (e == hipSuccess) e = launch_partial(plan->shape, plan->kind == 1, plan->units, pa, st);
+    if (e == hipSuccess && plan->prof_after) e = hipEventRecord(plan->prof_after, st);
     if (e != hipSuccess) return fail(BLOCKATTN_ERR_HIP, std::string("partial kernel launch: ") + hipGetErrorString(e));
 
     CombineArgs ca{};
@@ -367,6 +371,15 @@ int blockattn_plan_info(blockattn_plan_t plan, blockattn_plan_info_t* info) {
     info->row_waves = plan->shape.row_waves;
     info->uploaded = plan->uploaded ? 1 : 0;
     info->workspace_bytes = plan->lay.total;
+    return BLOCKATTN_OK;
+}
+
+int blockattn_plan_set_profile_events(blockattn_plan_t plan, void* before, void* after) {
+    if (!plan) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "plan is NULL");
+    if ((before == nullptr) != (after == nullptr))
+        return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "pass both profiling events or neither");
+    plan->prof_before = static_cast<hipEvent_t>(before);
+    plan->prof_after = static_cast<hipEvent_t>(after);
     return BLOCKATTN_OK;
 }
 
