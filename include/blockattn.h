@@ -93,6 +93,8 @@ typedef struct blockattn_plan_info {
     int32_t token_groups;      /* wavefronts streaming different tiles inside one workgroup */
     int32_t row_waves;         /* wavefronts sharing one tile, each owning some query rows */
     int32_t uploaded;          /* 1 once the work list has been copied into a workspace */
+    int32_t fused_combine;     /* 1: the last split of a (request, kv head) combines inside the attention
+                                  kernel; 0: a separate combine launch follows (many splits) */
     size_t workspace_bytes;    /* bytes the plan needs */
 } blockattn_plan_info_t;
 

@@ -66,6 +66,7 @@ class blockattn_plan_info_t(ctypes.Structure):
         ("token_groups", ctypes.c_int32),
         ("row_waves", ctypes.c_int32),
         ("uploaded", ctypes.c_int32),
+        ("fused_combine", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 

@@ -39,13 +39,17 @@ int fail(int code, const std::string& msg) {
 
 constexpr int kNumCUs = 256;
 constexpr size_t kLdsPerCU = 160 * 1024;
-constexpr int kMaxWavesPerCU = 16;
+constexpr int kMaxWavesPerCU = 8;  // two waves per SIMD at ~200 VGPRs
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Layout {
-    size_t work = 0, pairs = 0, m = 0, l = 0, acc = 0, total = 0;
+    size_t work = 0, pairs = 0, counters = 0, m = 0, l = 0, acc = 0, total = 0;
 };
+
+// The last unit to finish combines its request's splits when there are at most this
+// many; beyond it a separate combine launch spreads the work over one workgroup per row.
+constexpr int kFuseMaxSplits = 16;
 
 }  // namespace
 
@@ -55,6 +59,7 @@ struct blockattn_plan_s {
     int g = 1, R = 1, NB = 1;
     KernelShape shape{};
     bool merge_active = false;
+    bool fused = true;
     int units = 0, max_splits = 0;
     std::vector<WorkItem> work;
     std::vector<int32_t> pair_table;
@@ -124,27 +129,32 @@ int tiles_for(const blockattn_params* p, int n) {
     return (n + kTileTokens - 1) / kTileTokens - lo / kTileTokens;
 }
 
-KernelShape choose_shape(int D, int NB) {
+KernelShape choose_shape(int D, int NB, int R) {
     KernelShape s{};
     s.head_dim = D;
-    // D = 64: up to two 16-row blocks per wave, one wave per tile when R <= 32.
-    // D = 128: one row block per wave and at least two waves per tile, so no wave
-    // stages more than half of a 16 KiB tile in registers.
-    if (D == 64) {
-        s.nbw = NB <= 2 ? NB : 2;
-        s.row_waves = (NB + s.nbw - 1) / s.nbw;
+    if (D == 64 && NB <= 2) {
+        // one wave owns every row and streams its own tiles
+        s.stream = true;
+        s.nbw = NB;
+        s.row_waves = 1;
+        s.token_groups = 4;
+        s.cpw = 0;
     } else {
-        s.nbw = 1;
-        s.row_waves = std::max(2, NB);
+        // row-waves share each tile through LDS: two row blocks per wave for D = 64,
+        // one for D = 128, and at least two waves per tile so a wave stages at most
+        // half of a 16 KiB tile in registers
+        s.stream = false;
+        s.nbw = D == 64 ? 2 : 1;
+        s.row_waves = std::max(D == 64 ? 1 : 2, (NB + s.nbw - 1) / s.nbw);
+        s.token_groups = std::max(1, std::min(4, kMaxWaves / s.row_waves));
+        const int nch = D / 8;
+        const int need = (nch + s.row_waves - 1) / s.row_waves;
+        s.cpw = need <= 4 ? 4 : 8;
     }
-    s.token_groups = std::max(1, std::min(4, kMaxWaves / s.row_waves));
-    const int nch = D / 8;
-    const int need = (nch + s.row_waves - 1) / s.row_waves;
-    s.cpw = need <= 4 ? 4 : (need <= 8 ? 8 : 16);
-    s.lds_bytes = partial_lds_bytes(D, s.nbw, s.row_waves, s.token_groups);
+    s.lds_bytes = attention_lds_bytes(s, R);
     while (s.lds_bytes > kLdsPerCU && s.token_groups > 1) {
         --s.token_groups;
-        s.lds_bytes = partial_lds_bytes(D, s.nbw, s.row_waves, s.token_groups);
+        s.lds_bytes = attention_lds_bytes(s, R);
     }
     return s;
 }
@@ -157,7 +167,7 @@ int build_plan(const blockattn_params* p, const int32_t* lens, blockattn_plan_s*
     pl->g = p->num_q_heads / p->num_kv_heads;
     pl->R = p->block_size * pl->g;
     pl->NB = (pl->R + 15) / 16;
-    pl->shape = choose_shape(p->head_dim, pl->NB);
+    pl->shape = choose_shape(p->head_dim, pl->NB, pl->R);
     pl->merge_active = pl->kind == 1 && p->block_size > 1 && p->window_right != 0;
 
     const int B = p->batch, H = p->num_kv_heads;
@@ -194,11 +204,13 @@ int build_plan(const blockattn_params* p, const int32_t* lens, blockattn_plan_s*
     if (pl->work.size() > 0x7FFFFFFFu / 2)
         return fail(BLOCKATTN_ERR_UNSUPPORTED, "too many work units; lower batch or splits_override");
     pl->units = (int)pl->work.size();
+    pl->fused = pl->max_splits <= kFuseMaxSplits;
 
     Layout& L = pl->lay;
     L.work = 0;
     L.pairs = align_up(L.work + pl->work.size() * sizeof(WorkItem), 256);
-    L.m = align_up(L.pairs + pl->pair_table.size() * sizeof(int32_t), 256);
+    L.counters = align_up(L.pairs + pl->pair_table.size() * sizeof(int32_t), 256);
+    L.m = align_up(L.counters + (size_t)B * H * sizeof(int32_t), 256);
     L.l = align_up(L.m + (size_t)pl->units * pl->R * sizeof(float), 256);
     L.acc = align_up(L.l + (size_t)pl->units * pl->R * sizeof(float), 256);
     L.total = align_up(L.acc + (size_t)pl->units * pl->R * p->head_dim * sizeof(float), 256);
@@ -229,59 +241,47 @@ int run_forward(blockattn_plan_t plan, const void* q, const void* k, const void*
     char* base = static_cast<char*>(ws);
     hipStream_t st = static_cast<hipStream_t>(stream);
 
-    PartialArgs pa{};
-    pa.q = static_cast<const uint16_t*>(q);
-    pa.kc = static_cast<const uint16_t*>(k);
-    pa.vc = static_cast<const uint16_t*>(v);
-    pa.page_table = pt;
-    pa.seq_lens = lens;
-    pa.work = reinterpret_cast<const WorkItem*>(base + plan->lay.work);
-    pa.part_m = reinterpret_cast<float*>(base + plan->lay.m);
-    pa.part_l = reinterpret_cast<float*>(base + plan->lay.l);
-    pa.part_acc = reinterpret_cast<float*>(base + plan->lay.acc);
-    pa.K = p.block_size;
-    pa.Hq = p.num_q_heads;
-    pa.Hkv = p.num_kv_heads;
-    pa.g = plan->g;
-    pa.R = plan->R;
-    pa.P = p.page_size;
-    pa.stride = p.page_table_stride;
-    pa.num_pages = p.num_pages;
-    pa.window_left = p.window_left;
-    pa.row_waves = plan->shape.row_waves;
-    pa.token_groups = plan->shape.token_groups;
-    pa.scale_log2 = (float)((double)p.sm_scale * 1.4426950408889634);
+    KernelArgs ka{};
+    ka.q = static_cast<const uint16_t*>(q);
+    ka.kc = static_cast<const uint16_t*>(k);
+    ka.vc = static_cast<const uint16_t*>(v);
+    ka.page_table = pt;
+    ka.seq_lens = lens;
+    ka.work = reinterpret_cast<const WorkItem*>(base + plan->lay.work);
+    ka.pair_table = reinterpret_cast<const int32_t*>(base + plan->lay.pairs);
+    ka.counters = reinterpret_cast<int32_t*>(base + plan->lay.counters);
+    ka.part_m = reinterpret_cast<float*>(base + plan->lay.m);
+    ka.part_l = reinterpret_cast<float*>(base + plan->lay.l);
+    ka.part_acc = reinterpret_cast<float*>(base + plan->lay.acc);
+    ka.out = static_cast<uint16_t*>(out);
+    ka.lse = lse;
+    ka.K = p.block_size;
+    ka.Hq = p.num_q_heads;
+    ka.Hkv = p.num_kv_heads;
+    ka.g = plan->g;
+    ka.R = plan->R;
+    ka.P = p.page_size;
+    ka.stride = p.page_table_stride;
+    ka.num_pages = p.num_pages;
+    ka.window_left = p.window_left;
+    ka.window_right = p.window_right;
+    ka.row_waves = plan->shape.row_waves;
+    ka.token_groups = plan->shape.token_groups;
+    ka.fused = plan->fused ? 1 : 0;
+    ka.merge = plan->merge_active ? 1 : 0;
+    ka.scale_log2 = (float)((double)p.sm_scale * 1.4426950408889634);
+
     hipError_t e = hipSuccess;
     if (plan->prof_before) e = hipEventRecord(plan->prof_before, st);
-    if (e == hipSuccess) e = launch_partial(plan->shape, plan->kind == 1, plan->units, pa, st);
+    if (e == hipSuccess) e = launch_attention(plan->shape, plan->kind == 1, plan->units, ka, st);
     if (e == hipSuccess && plan->prof_after) e = hipEventRecord(plan->prof_after, st);
-    if (e != hipSuccess) return fail(BLOCKATTN_ERR_HIP, std::string("partial kernel launch: ") + hipGetErrorString(e));
-
-    CombineArgs ca{};
-    ca.q = pa.q;
-    ca.kc = pa.kc;
-    ca.vc = pa.vc;
-    ca.page_table = pt;
-    ca.seq_lens = lens;
-    ca.pair_table = reinterpret_cast<const int32_t*>(base + plan->lay.pairs);
-    ca.part_m = pa.part_m;
-    ca.part_l = pa.part_l;
-    ca.part_acc = pa.part_acc;
-    ca.out = static_cast<uint16_t*>(out);
-    ca.lse = lse;
-    ca.K = p.block_size;
-    ca.Hq = p.num_q_heads;
-    ca.Hkv = p.num_kv_heads;
-    ca.g = plan->g;
-    ca.R = plan->R;
-    ca.P = p.page_size;
-    ca.stride = p.page_table_stride;
-    ca.num_pages = p.num_pages;
-    ca.window_right = p.window_right;
-    ca.scale_log2 = pa.scale_log2;
-    const int rows = p.batch * p.num_kv_heads * plan->R;
-    e = launch_combine(p.head_dim, plan->merge_active, rows, ca, st);
-    if (e != hipSuccess) return fail(BLOCKATTN_ERR_HIP, std::string("combine kernel launch: ") + hipGetErrorString(e));
+    if (e != hipSuccess) return fail(BLOCKATTN_ERR_HIP, std::string("attention kernel launch: ") + hipGetErrorString(e));
+    if (!plan->fused && plan->max_splits > 1) {
+        const int rows = p.batch * p.num_kv_heads * plan->R;
+        e = launch_combine(p.head_dim, rows, ka, st);
+        if (e != hipSuccess)
+            return fail(BLOCKATTN_ERR_HIP, std::string("combine kernel launch: ") + hipGetErrorString(e));
+    }
     return BLOCKATTN_OK;
 }
 
@@ -318,7 +318,7 @@ int blockattn_plan(const blockattn_params* params, const int32_t* seq_lens_host,
             delete pl;
             return fail(BLOCKATTN_ERR_WORKSPACE_TOO_SMALL, buf);
         }
-        const size_t head = pl->lay.m;  // work list + pair table
+        const size_t head = pl->lay.m;  // work list, pair table and zeroed split counters
         hipError_t e = hipHostMalloc(&pl->stage, head, hipHostMallocDefault);
         if (e != hipSuccess) {
             delete pl;
@@ -370,6 +370,7 @@ int blockattn_plan_info(blockattn_plan_t plan, blockattn_plan_info_t* info) {
     info->token_groups = plan->shape.token_groups;
     info->row_waves = plan->shape.row_waves;
     info->uploaded = plan->uploaded ? 1 : 0;
+    info->fused_combine = plan->fused ? 1 : 0;
     info->workspace_bytes = plan->lay.total;
     return BLOCKATTN_OK;
 }

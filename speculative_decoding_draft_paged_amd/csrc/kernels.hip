@@ -1,36 +1,42 @@
 // gfx950 kernels for draft-block paged attention.
 //
-// partial_kernel (split-KV partial attention). One workgroup = one work unit:
-//   a range of 32-token key tiles of one (request b, kv head). Its waves form
-//   WT "token groups" that stream different tiles, and each token group has WR
-//   "row waves" that share one tile through LDS and own NBW 16-row blocks of the
-//   R = K * group query rows each. Per tile:
-//     - the K and V slabs (32 rows x D, contiguous inside an HND page) come in as
-//       coalesced 16-byte global loads, one tile ahead in registers, and are
-//       written to a double-buffered LDS tile (K row-major, V transposed so the
-//       tokens become the MFMA reduction dimension);
-//     - S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (tokens are the M dimension, the
-//       query rows the N dimension, so each lane owns one query row of S^T and
-//       the softmax statistics stay in-lane);
-//     - online softmax in exp2 space (scores pre-multiplied by sm_scale*log2 e),
-//       masks only on edge tiles; V rows past the sequence end are zeroed by
-//       select, so stale cache slots (even NaN) cannot leak through 0 * NaN;
-//     - O^T += V^T P^T on the same MFMA with P rounded to bf16; the P operand is
-//       exactly the lane's own S^T accumulator registers (no shuffles).
-//   At the end the token groups merge through LDS and the unit writes fp32
-//   partial (acc, m, l). This is the split-KV ("flash-decoding") partial step
-//   of TensorRT-LLM PR #16150 (paged DFlash cross-attention, commit "rework
-//   flash-decoding style") and the multi-CTA split-KV of PR #20374, redone
-//   for 64-wide wavefronts, MFMA tiles and HND pages.
+// attention kernels (split-KV partial attention with a fused epilogue). One
+// workgroup = one work unit: a range of 32-token key tiles of one (request b,
+// kv head). Per tile:
+//   - S^T = K Q^T on v_mfma_f32_16x16x32_bf16. Tokens are the M dimension and
+//     the query rows the N dimension, so every lane owns one query row of S^T
+//     and the softmax statistics stay in-lane;
+//   - online softmax in exp2 space (scores pre-multiplied by sm_scale*log2 e),
+//     masks only on edge tiles; V rows past the sequence end are zeroed by
+//     select, so stale cache slots (even NaN) cannot leak through 0 * NaN;
+//   - O^T += V^T P^T on the same MFMA with P rounded to bf16; the P operand is
+//     exactly the lane's own S^T accumulator registers (no shuffles). V^T comes
+//     from a row-major V tile in LDS through the transposing LDS read.
+// Two main loops share that tile step:
+//   stream_kernel (R <= 32 rows, one wave owns every row): each wave streams its
+//     own tiles with no workgroup barrier. K goes straight from HBM into the
+//     MFMA A fragments; V goes row-major into a private LDS tile. Two tiles are
+//     in flight per wave, and the page ids of the wave's next 64 half-tiles sit
+//     in one VGPR, read with readlane, so no scalar load sits on the path.
+//   shared_kernel (large R): WR row-waves share each tile through a double-
+//     buffered LDS copy and own some 16-row blocks each.
+// Epilogue: the token groups of the workgroup merge through LDS. A unit that is
+// its request's only split writes the final bf16 output and base-2 LSE itself.
+// Otherwise it writes its fp32 (acc, m, l); with the fused combine the last
+// unit of the (request, kv head) to finish (an agent-scope counter) combines
+// all splits and writes the result. The windowed form then folds in the block
+// keys after each query by the LSE merge (TensorRT-LLM PR #21130, Description
+// item 1 and its formulation table: lse = lse_c (+) lse_f, out = out_c +
+// w (out_f - out_c), w = 2^(lse_f - lse)).
 //
-// combine_kernel (LSE combine over the splits, plus the fused future-block-key
-//   merge of the windowed form). One workgroup per output row (b, i, h).
-//   M = max_s m_s, w_s = 2^(m_s - M), out = sum w_s acc_s / sum w_s l_s,
-//   lse2 = M + log2(sum w_s l_s). For the windowed form it then scores the block
-//   keys after the query (at most K - 1, read from the paged cache), forms their
-//   (out_f, lse_f) and merges: lse = lse_c (+) lse_f, out = out_c + w (out_f -
-//   out_c) with w = 2^(lse_f - lse), the sigmoid/lerp form of PR #21130's merge
-//   formulation table. It writes bf16 out (round to nearest even) and fp32 lse.
+// combine_kernel: the same combine and merge as a separate launch, one
+// workgroup per output row, for plans with many splits per request (small batch,
+// long context), where one workgroup per request would serialise the combine.
+//
+// The split-KV form itself follows the flash-decoding rework of TensorRT-LLM
+// PR #16150 (paged DFlash cross-attention, commits "rework flash-decoding style"
+// and "split count as a runtime argument") and the multi-CTA split-KV of
+// PR #20374, redone for 64-wide wavefronts, MFMA tiles and HND pages.
 #include "internal.h"
 
 #include <math.h>
@@ -42,8 +48,10 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int T = kTileTokens;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -58,157 +66,105 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_floa
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
-template <int D, int NBW, int CPW, bool WINDOWED>
-__global__ __launch_bounds__(512) void partial_kernel(const PartialArgs a) {
-    constexpr int T = kTileTokens;
-    constexpr int KP = D + 8;  // padded pitch of the K tile (bf16 elements)
-    constexpr int VP = T + 8;  // padded pitch of the transposed V tile
-    constexpr int KT = T * KP;
-    constexpr int BUF = KT + D * VP;
-    constexpr int NCH = D / 8;           // 1-KiB chunks of a tile, K then V
-    constexpr int HALF = NCH / 2;        // chunks per tensor
-    constexpr int RPC = 1024 / (2 * D);  // tile rows per chunk
-    constexpr int DB = D / 16;           // 16-wide d blocks of O^T
-    constexpr int KK = D / 32;           // 32-deep k steps of S^T
+__device__ __forceinline__ u32x4_t ldg16(const uint16_t* p) { return *(const u32x4_t*)p; }
 
-    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int WR = a.row_waves, WT = a.token_groups;
-    const int tg = wave / WR;
-    const int wr = wave - tg * WR;
-    const int r16 = lane & 15, quad = lane >> 4;
-    uint16_t* tg_lds = lds + (size_t)tg * 2 * BUF;
+// Transposing LDS read (ds_read_b64_tr_b16). Within each 16-lane group, lane l
+// receives element l % 4 of the 8 bytes addressed by lane 4e + (l % 16) / 4, for
+// e = 0..3. With lane l pointing at row l/4, columns 4(l%4)..+3 of a row-major
+// 4 x 16 block, lane l gets column l of that block (4 rows).
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
+    i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p));
+    return __builtin_bit_cast(u32x2_t, v);
+}
 
+struct Unit {
+    int b, hk, s, S, N, C, ulo, uhi;
+};
+
+template <bool WINDOWED>
+__device__ __forceinline__ Unit decode_unit(const KernelArgs& a) {
     const WorkItem wi = a.work[blockIdx.x];
-    const int b = wi.b, hk = wi.hk;
-    const int N = clampi(a.seq_lens[b], a.K, a.stride * a.P);
-    const int C = N - a.K;
-    const bool left_win = WINDOWED && a.window_left > 0;
-    const int key_lo = left_win ? max(0, C - a.window_left + 1) : 0;
-    const int tb = key_lo / T, te = (N + T - 1) / T, nt = te - tb;
-    const int ulo = tb + (int)((int64_t)wi.s * nt / wi.S);
-    const int uhi = tb + (int)((int64_t)(wi.s + 1) * nt / wi.S);
+    Unit u;
+    u.b = wi.b;
+    u.hk = wi.hk;
+    u.s = wi.s;
+    u.S = wi.S;
+    u.N = clampi(a.seq_lens[wi.b], a.K, a.stride * a.P);
+    u.C = u.N - a.K;
+    const int key_lo = (WINDOWED && a.window_left > 0) ? max(0, u.C - a.window_left + 1) : 0;
+    const int tb = key_lo / T, te = (u.N + T - 1) / T, nt = te - tb;
+    u.ulo = tb + (int)((int64_t)wi.s * nt / wi.S);
+    u.uhi = tb + (int)((int64_t)(wi.s + 1) * nt / wi.S);
+    return u;
+}
 
-    // Query fragments (B operand of S^T = K Q^T) and per-row key bounds.
+// Per-wave query fragments (B operand of S^T = K Q^T), row key bounds and softmax state.
+template <int D, int NBW, bool WINDOWED>
+struct WaveRows {
+    static constexpr int KK = D / 32, DB = D / 16;
     bf16x8_t qf[NBW][KK];
     int row_lo[NBW], row_hi[NBW];
-    bool blk_on[NBW];
-#pragma unroll
-    for (int n = 0; n < NBW; ++n) {
-        const int nb = wr * NBW + n;
-        const int r = nb * 16 + r16;
-        blk_on[n] = nb * 16 < a.R;
-        const bool live = r < a.R;
-        const int i = live ? r / a.g : a.K - 1;
-        const int l = live ? r - (r / a.g) * a.g : 0;
-        const uint16_t* qrow = a.q + ((size_t)(b * a.K + i) * a.Hq + hk * a.g + l) * D;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            u32x4_t v = live ? *(const u32x4_t*)(qrow + kk * 32 + quad * 8) : u32x4_t{0u, 0u, 0u, 0u};
-            qf[n][kk] = __builtin_bit_cast(bf16x8_t, v);
-        }
-        const int p = C + i;
-        row_lo[n] = left_win ? max(0, p - a.window_left + 1) : 0;
-        row_hi[n] = WINDOWED ? p : N - 1;
-    }
-    const int lo_max = left_win ? max(0, C + a.K - a.window_left) : 0;
-    const int hi_min = WINDOWED ? C : N - 1;
-
+    bool on[NBW];
     f32x4_t acc[NBW][DB];
-    float m_run[NBW], l_run[NBW];
+    float m[NBW], l[NBW];
+    int lo_max, hi_min;
+
+    __device__ __forceinline__ void init(const KernelArgs& a, const Unit& u, int first_block, int lane) {
+        const int r16 = lane & 15, quad = lane >> 4;
+        const bool left_win = WINDOWED && a.window_left > 0;
 #pragma unroll
-    for (int n = 0; n < NBW; ++n) {
-        m_run[n] = kNegInf;
-        l_run[n] = 0.f;
+        for (int n = 0; n < NBW; ++n) {
+            const int nb = first_block + n;
+            const int r = nb * 16 + r16;
+            on[n] = nb * 16 < a.R;
+            const bool live = r < a.R;
+            const int i = live ? r / a.g : a.K - 1;
+            const int lg = live ? r - (r / a.g) * a.g : 0;
+            const uint16_t* qrow = a.q + ((size_t)(u.b * a.K + i) * a.Hq + u.hk * a.g + lg) * D;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) acc[n][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int kk = 0; kk < KK; ++kk)
+                qf[n][kk] = __builtin_bit_cast(bf16x8_t, live ? ldg16(qrow + kk * 32 + quad * 8)
+                                                              : u32x4_t{0u, 0u, 0u, 0u});
+            const int p = u.C + i;
+            row_lo[n] = left_win ? max(0, p - a.window_left + 1) : 0;
+            row_hi[n] = WINDOWED ? p : u.N - 1;
+            m[n] = kNegInf;
+            l[n] = 0.f;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) acc[n][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        lo_max = left_win ? max(0, u.C + a.K - a.window_left) : 0;
+        hi_min = WINDOWED ? u.C : u.N - 1;
     }
 
-    const int32_t* pt_row = a.page_table + (size_t)b * a.stride;
-    const int last_page = (N - 1) / a.P;
-    const size_t head_elems = (size_t)a.P * D;
-    u32x4_t pre[CPW];
-
-    // Issue the global loads of one tile into registers. Each 16-token half of the
-    // tile is contiguous inside one page; a chunk never straddles the halves.
-    auto prefetch = [&](int tile) {
-        const int t0 = tile * T;
-        const int lp0 = min(t0 / a.P, last_page);
-        const int lp1 = min((t0 + 16) / a.P, last_page);
-        const int pid0 = clampi(pt_row[lp0], 0, a.num_pages - 1);
-        const int pid1 = clampi(pt_row[lp1], 0, a.num_pages - 1);
-        const size_t base0 = ((size_t)pid0 * a.Hkv + hk) * head_elems + (size_t)(t0 % a.P) * D;
-        const size_t base1 = ((size_t)pid1 * a.Hkv + hk) * head_elems + (size_t)((t0 + 16) % a.P) * D;
+    // Scores of one tile for every owned row block.
+    __device__ __forceinline__ void scores(const bf16x8_t (&kf)[2][KK], f32x4_t (&s)[NBW][2]) const {
 #pragma unroll
-        for (int ci = 0; ci < CPW; ++ci) {
-            const int c = wr + ci * WR;
-            if (c < NCH) {
-                const bool is_v = c >= HALF;
-                const int cc = is_v ? c - HALF : c;
-                const int off = cc * 512 + lane * 8;  // bf16 elements inside the tensor tile
-                const int row = off / D, col = off - (off / D) * D;
-                const bool h1 = row >= 16;
-                const size_t base = (h1 ? base1 : base0) + (size_t)(row - (h1 ? 16 : 0)) * D + col;
-                pre[ci] = *(const u32x4_t*)((is_v ? a.vc : a.kc) + base);
-            }
-        }
-    };
-
-    // Move the prefetched registers of one tile into an LDS buffer.
-    auto store = [&](int tile, uint16_t* buf) {
-        const int t0 = tile * T;
+        for (int n = 0; n < NBW; ++n) {
 #pragma unroll
-        for (int ci = 0; ci < CPW; ++ci) {
-            const int c = wr + ci * WR;
-            if (c < NCH) {
-                const int cc = c < HALF ? c : c - HALF;
-                const int off = cc * 512 + lane * 8;
-                const int row = off / D, col = off - (off / D) * D;
-                if (c < HALF) {
-                    *(u32x4_t*)(buf + row * KP + col) = pre[ci];
-                } else {
-                    const u32x4_t v = (t0 + row < N) ? pre[ci] : u32x4_t{0u, 0u, 0u, 0u};
-                    uint16_t* vt = buf + KT + col * VP + row;
+            for (int mb = 0; mb < 2; ++mb) {
+                s[n][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                if (on[n]) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) vt[e * VP] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+                    for (int kk = 0; kk < KK; ++kk)
+                        s[n][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mb][kk], qf[n][kk], s[n][mb], 0, 0, 0);
                 }
             }
         }
-    };
+    }
 
-    auto compute = [&](int tile, const uint16_t* buf) {
-        const int t0 = tile * T;
-        bf16x8_t kf[2][KK];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-                kf[mb][kk] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(buf + (mb * 16 + r16) * KP + kk * 32 + quad * 8));
-        bf16x8_t vf[DB];
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const uint16_t* vrow = buf + KT + (db * 16 + r16) * VP;
-            const u32x2_t lo = *(const u32x2_t*)(vrow + 4 * quad);
-            const u32x2_t hi = *(const u32x2_t*)(vrow + 16 + 4 * quad);
-            vf[db] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
-        }
+    // Online softmax update and O^T += V^T P^T for one tile starting at token t0.
+    __device__ __forceinline__ void update(const f32x4_t (&s)[NBW][2], const bf16x8_t (&vf)[DB], int t0, float scale,
+                                           int quad) {
         const bool edge = (t0 < lo_max) || (t0 + T - 1 > hi_min);
 #pragma unroll
         for (int n = 0; n < NBW; ++n) {
-            if (!blk_on[n]) continue;
-            f32x4_t s[2];
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                s[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk) s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mb][kk], qf[n][kk], s[mb], 0, 0, 0);
-            }
+            if (!on[n]) continue;
             float x[8];
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) x[mb * 4 + j] = s[mb][j] * a.scale_log2;
+                for (int j = 0; j < 4; ++j) x[mb * 4 + j] = s[n][mb][j] * scale;
             if (edge) {
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
@@ -223,105 +179,426 @@ __global__ __launch_bounds__(512) void partial_kernel(const PartialArgs a) {
             for (int k = 1; k < 8; ++k) mx = fmaxf(mx, x[k]);
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run[n], mx);
+            const float m_new = fmaxf(m[n], mx);
             const float m_use = m_new == kNegInf ? 0.f : m_new;
-            const float alpha = fast_exp2(m_run[n] - m_use);
-            float p[8];
+            const float alpha = fast_exp2(m[n] - m_use);
+            bf16x8_t pb;
             float psum = 0.f;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                p[k] = fast_exp2(x[k] - m_use);
-                psum += p[k];
+                const float p = fast_exp2(x[k] - m_use);
+                psum += p;
+                pb[k] = (__bf16)p;
             }
-            l_run[n] = l_run[n] * alpha + psum;
-            m_run[n] = m_new;
-            bf16x8_t pb;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) pb[k] = (__bf16)p[k];
+            l[n] = l[n] * alpha + psum;
+            m[n] = m_new;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 acc[n][db] *= alpha;
                 acc[n][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pb, acc[n][db], 0, 0, 0);
             }
         }
-    };
-
-    const int n_iter = uhi > ulo ? (uhi - ulo + WT - 1) / WT : 0;
-    int tile = ulo + tg;
-    if (n_iter > 0 && tile < uhi) prefetch(tile);
-    for (int it = 0; it < n_iter; ++it) {
-        uint16_t* buf = tg_lds + (it & 1) * BUF;
-        const bool valid = tile < uhi;
-        if (valid) store(tile, buf);
-        __syncthreads();
-        const int next = tile + WT;
-        if (next < uhi) prefetch(next);
-        if (valid) compute(tile, buf);
-        tile = next;
     }
+};
 
-    // Row sums were kept per lane; the four lanes of a row hold disjoint tokens.
+// Floats of LDS the epilogue needs (it reuses the tile buffers).
+__host__ __device__ constexpr size_t epilogue_floats(int D, int slots_per_group, int token_groups) {
+    return (size_t)token_groups * slots_per_group * 16 * (D + 4) + 2 * 128 + 128 * kMaxFuture + 4;
+}
+
+// Merge the wave states of a workgroup, then write a partial, or (only split /
+// last arriver) the final bf16 output and LSE, with the windowed merge.
+template <int D, int NBW, bool WINDOWED>
+__device__ void finish_unit(const KernelArgs& a, const Unit& u, WaveRows<D, NBW, WINDOWED>& w, int tg, int wr,
+                            int WT, int WR, float* lds) {
+    constexpr int DB = D / 16, MP = D + 4;
+    const int tid = threadIdx.x, nthreads = blockDim.x;
+    const int lane = tid & 63, r16 = lane & 15, quad = lane >> 4;
+    const int R = a.R;
+    const int slots = WR * NBW;
+    float* mg = lds;
+    float* rowM = mg + (size_t)WT * slots * 16 * MP;
+    float* rowL = rowM + 128;
+    float* sf = rowL + 128;
+    int* flag = reinterpret_cast<int*>(sf + 128 * kMaxFuture);
+
 #pragma unroll
     for (int n = 0; n < NBW; ++n) {
-        l_run[n] += __shfl_xor(l_run[n], 16);
-        l_run[n] += __shfl_xor(l_run[n], 32);
+        w.l[n] += __shfl_xor(w.l[n], 16);
+        w.l[n] += __shfl_xor(w.l[n], 32);
     }
-
-    // Merge the token groups through LDS and write this unit's partial state.
-    constexpr int MP = D + 4;  // floats per row slot: acc[D], m, l, pad
-    __syncthreads();
-    float* mg = reinterpret_cast<float*>(lds);
+    __syncthreads();  // tile buffers are free from here on
 #pragma unroll
     for (int n = 0; n < NBW; ++n) {
-        float* slot = mg + ((size_t)((tg * WR + wr) * NBW + n) * 16 + r16) * MP;
+        float* slot = mg + ((size_t)(tg * slots + wr * NBW + n) * 16 + r16) * MP;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) *(f32x4_t*)(slot + db * 16 + quad * 4) = acc[n][db];
+        for (int db = 0; db < DB; ++db) *(f32x4_t*)(slot + db * 16 + quad * 4) = w.acc[n][db];
         if (quad == 0) {
-            slot[D] = m_run[n];
-            slot[D + 1] = l_run[n];
+            slot[D] = w.m[n];
+            slot[D + 1] = w.l[n];
         }
     }
     __syncthreads();
-    const size_t unit_row0 = (size_t)blockIdx.x * a.R;
-    const int per_tg = WR * NBW * 16 * MP;
-    for (int idx = threadIdx.x; idx < a.R * D; idx += blockDim.x) {
-        const int r = idx / D, d = idx - (idx / D) * D;
-        const int nb = r >> 4;
-        const int wr_r = nb / NBW, n_r = nb - wr_r * NBW;
-        const int off = ((wr_r * NBW + n_r) * 16 + (r & 15)) * MP;
+    // Row r of token group t sits at mg[(t * slots * 16 + r) * MP].
+    const size_t tg_stride = (size_t)slots * 16 * MP;
+    for (int r = tid; r < R; r += nthreads) {
         float M = kNegInf;
-        for (int t = 0; t < WT; ++t) M = fmaxf(M, mg[t * per_tg + off + D]);
-        float L = 0.f, A = 0.f;
-        if (M != kNegInf) {
-            for (int t = 0; t < WT; ++t) {
-                const float w = fast_exp2(mg[t * per_tg + off + D] - M);
-                L += w * mg[t * per_tg + off + D + 1];
-                A += w * mg[t * per_tg + off + d];
+        for (int t = 0; t < WT; ++t) M = fmaxf(M, mg[t * tg_stride + (size_t)r * MP + D]);
+        float L = 0.f;
+        if (M != kNegInf)
+            for (int t = 0; t < WT; ++t)
+                L += fast_exp2(mg[t * tg_stride + (size_t)r * MP + D] - M) * mg[t * tg_stride + (size_t)r * MP + D + 1];
+        rowM[r] = M;
+        rowL[r] = L;
+    }
+    __syncthreads();
+    if (WT > 1) {
+        for (int idx = tid; idx < R * D; idx += nthreads) {
+            const int r = idx / D, d = idx - (idx / D) * D;
+            const float M = rowM[r];
+            float A = 0.f;
+            if (M != kNegInf)
+                for (int t = 0; t < WT; ++t)
+                    A += fast_exp2(mg[t * tg_stride + (size_t)r * MP + D] - M) * mg[t * tg_stride + (size_t)r * MP + d];
+            mg[(size_t)r * MP + d] = A;
+        }
+        __syncthreads();
+    }
+
+    const int pair = u.b * a.Hkv + u.hk;
+    if (u.S > 1) {
+        const size_t row0 = (size_t)blockIdx.x * R;
+        for (int idx = tid; idx < R * (D / 4); idx += nthreads) {
+            const int r = idx / (D / 4), d4 = idx - (idx / (D / 4)) * (D / 4);
+            *(f32x4_t*)(a.part_acc + (row0 + r) * D + 4 * d4) = *(const f32x4_t*)(mg + (size_t)r * MP + 4 * d4);
+        }
+        for (int r = tid; r < R; r += nthreads) {
+            a.part_m[row0 + r] = rowM[r];
+            a.part_l[row0 + r] = rowL[r];
+        }
+        if (!a.fused) return;
+        // Publish this unit's partial at agent scope, then count it. The unit that
+        // brings the count to S combines; it also resets the counter for the next call.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __syncthreads();
+        if (tid == 0) {
+            const int prev = __hip_atomic_fetch_add(a.counters + pair, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            const int last = prev == u.S - 1;
+            if (last) __hip_atomic_store(a.counters + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *flag = last;
+        }
+        __syncthreads();
+        if (!*flag) return;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        const int u0 = a.pair_table[2 * pair];
+        for (int r = tid; r < R; r += nthreads) {
+            float M = kNegInf;
+            for (int s = 0; s < u.S; ++s) M = fmaxf(M, a.part_m[(size_t)(u0 + s) * R + r]);
+            float L = 0.f;
+            if (M != kNegInf)
+                for (int s = 0; s < u.S; ++s)
+                    L += fast_exp2(a.part_m[(size_t)(u0 + s) * R + r] - M) * a.part_l[(size_t)(u0 + s) * R + r];
+            rowM[r] = M;
+            rowL[r] = L;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < R * (D / 4); idx += nthreads) {
+            const int r = idx / (D / 4), d4 = idx - (idx / (D / 4)) * (D / 4);
+            const float M = rowM[r];
+            f32x4_t A = {0.f, 0.f, 0.f, 0.f};
+            if (M != kNegInf)
+                for (int s = 0; s < u.S; ++s) {
+                    const size_t pr = (size_t)(u0 + s) * R + r;
+                    A += fast_exp2(a.part_m[pr] - M) * *(const f32x4_t*)(a.part_acc + pr * D + 4 * d4);
+                }
+            *(f32x4_t*)(mg + (size_t)r * MP + 4 * d4) = A;
+        }
+        __syncthreads();
+    }
+
+    // Final stage: out = acc / L, lse = M + log2 L, then the future-block-key merge.
+    const int32_t* pt_row = a.page_table + (size_t)u.b * a.stride;
+    if (a.merge) {
+        const int nw = nthreads >> 6, wv = tid >> 6;
+        for (int r = wv; r < R; r += nw) {
+            const int i = r / a.g, h = u.hk * a.g + (r - (r / a.g) * a.g);
+            const int p = u.C + i;
+            const int f_hi = a.window_right < 0 ? u.N - 1 : min(u.N - 1, p + a.window_right);
+            const uint16_t* qrow = a.q + ((size_t)(u.b * a.K + i) * a.Hq + h) * D;
+            for (int f = 0; f < f_hi - p; ++f) {
+                const int j = p + 1 + f;
+                const int pid = clampi(pt_row[j / a.P], 0, a.num_pages - 1);
+                const uint16_t* krow = a.kc + (((size_t)pid * a.Hkv + u.hk) * a.P + (j % a.P)) * D;
+                float dot = 0.f;
+                for (int d = lane; d < D; d += 64) dot += bf16_to_f32(qrow[d]) * bf16_to_f32(krow[d]);
+                for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+                if (lane == 0) sf[r * kMaxFuture + f] = dot * a.scale_log2;
             }
         }
-        a.part_acc[(unit_row0 + r) * D + d] = A;
-        if (d == 0) {
-            a.part_m[unit_row0 + r] = M;
-            a.part_l[unit_row0 + r] = L;
+        __syncthreads();
+    }
+    for (int idx = tid; idx < R * D; idx += nthreads) {
+        const int r = idx / D, d = idx - (idx / D) * D;
+        const int i = r / a.g, h = u.hk * a.g + (r - (r / a.g) * a.g);
+        const float M = rowM[r], L = rowL[r];
+        float o = L > 0.f ? mg[(size_t)r * MP + d] / L : 0.f;
+        float lse = L > 0.f ? M + log2f(L) : kNegInf;
+        if (a.merge) {
+            const int p = u.C + i;
+            const int f_hi = a.window_right < 0 ? u.N - 1 : min(u.N - 1, p + a.window_right);
+            const int nf = f_hi - p;
+            if (nf > 0) {
+                const float* srow = sf + r * kMaxFuture;
+                float mf = kNegInf;
+                for (int f = 0; f < nf; ++f) mf = fmaxf(mf, srow[f]);
+                float z = 0.f;
+                for (int f = 0; f < nf; ++f) z += fast_exp2(srow[f] - mf);
+                const float lse_f = mf + log2f(z);
+                float of = 0.f;
+                for (int f = 0; f < nf; ++f) {
+                    const int j = p + 1 + f;
+                    const int pid = clampi(pt_row[j / a.P], 0, a.num_pages - 1);
+                    of += fast_exp2(srow[f] - lse_f) *
+                          bf16_to_f32(a.vc[(((size_t)pid * a.Hkv + u.hk) * a.P + (j % a.P)) * D + d]);
+                }
+                const float hi2 = fmaxf(lse, lse_f), lo2 = fminf(lse, lse_f);
+                const float merged = hi2 + log2f(1.f + fast_exp2(lo2 - hi2));
+                o = o + fast_exp2(lse_f - merged) * (of - o);
+                lse = merged;
+            }
         }
+        const size_t orow = (size_t)(u.b * a.K + i) * a.Hq + h;
+        a.out[orow * D + d] = f32_to_bf16_rne(o);
+        if (d == 0 && a.lse) a.lse[orow] = lse;
     }
 }
 
-template <int D, bool MERGE>
-__global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
+// ---------------------------------------------------------------------------------
+// Streaming main loop: one wave owns every row (R <= 16 * NBW), WT waves per
+// workgroup stream interleaved tiles of the unit, two tiles in flight per wave.
+template <int D, int NBW, bool WINDOWED>
+__global__ __launch_bounds__(512) void stream_kernel(const KernelArgs a) {
+    constexpr int KK = D / 32, DB = D / 16;
+    constexpr int VCH = D / 16;  // 1-KiB chunks of the V tile (16 bytes per lane each)
+    constexpr int VP = D + 8;    // padded row pitch of the V tile in LDS (bf16 elements)
+    constexpr int RPC = 512 / D; // tile rows per chunk
+
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, quad = lane >> 4;
+    const int WT = a.token_groups;
+    const Unit u = decode_unit<WINDOWED>(a);
+    WaveRows<D, NBW, WINDOWED> w;
+    w.init(a, u, 0, lane);
+    uint16_t* vlds = lds + (size_t)wave * T * VP;
+
+    const int span = u.uhi - u.ulo;
+    const int nk = span > wave ? (span - wave + WT - 1) / WT : 0;
+    const int32_t* pt_row = a.page_table + (size_t)u.b * a.stride;
+    const int last_page = (u.N - 1) / a.P;
+    const size_t head_elems = (size_t)a.P * D;
+
+    // Page ids of the wave's tiles kb .. kb+31 (lane 2j + h: half h of tile kb + j),
+    // and of the 32 tiles after them.
+    auto load_pids = [&](int kbase) {
+        const int k = kbase + (lane >> 1);
+        if (k >= nk) return 0;
+        const int tok = (u.ulo + wave + k * WT) * T + 16 * (lane & 1);
+        return clampi(pt_row[min(tok / a.P, last_page)], 0, a.num_pages - 1);
+    };
+    int kb = 0;
+    int pid_cur = load_pids(0);
+    int pid_nxt = load_pids(32);
+
+    struct TileRegs {
+        u32x4_t k[2][KK];
+        u32x4_t v[VCH];
+    };
+    auto issue = [&](TileRegs& t, int k) {
+        const int j = 2 * (k - kb);
+        const int pid0 = j < 64 ? __builtin_amdgcn_readlane(pid_cur, j) : __builtin_amdgcn_readlane(pid_nxt, j - 64);
+        const int pid1 = j < 64 ? __builtin_amdgcn_readlane(pid_cur, j + 1)
+                                : __builtin_amdgcn_readlane(pid_nxt, j - 63);
+        const int t0 = (u.ulo + wave + k * WT) * T;
+        const size_t base0 = ((size_t)pid0 * a.Hkv + u.hk) * head_elems + (size_t)(t0 % a.P) * D;
+        const size_t base1 = ((size_t)pid1 * a.Hkv + u.hk) * head_elems + (size_t)((t0 + 16) % a.P) * D;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                t.k[mb][kk] = ldg16(a.kc + (mb ? base1 : base0) + (size_t)r16 * D + kk * 32 + quad * 8);
+#pragma unroll
+        for (int c = 0; c < VCH; ++c) {
+            const int row = c * RPC + (lane * 8) / D;  // tile row of this lane's 16 bytes
+            const int col = (lane * 8) % D;
+            const bool h1 = c * RPC >= 16;
+            t.v[c] = ldg16(a.vc + (h1 ? base1 : base0) + (size_t)(row - (h1 ? 16 : 0)) * D + col);
+        }
+    };
+
+    auto consume = [&](TileRegs& t, int k) {
+        if (k - kb == 32) {  // slide the page-id window
+            kb += 32;
+            pid_cur = pid_nxt;
+            pid_nxt = load_pids(kb + 32);
+        }
+        const int t0 = (u.ulo + wave + k * WT) * T;
+#pragma unroll
+        for (int c = 0; c < VCH; ++c) {
+            const int row = c * RPC + (lane * 8) / D;
+            const int col = (lane * 8) % D;
+            *(u32x4_t*)(vlds + row * VP + col) = (t0 + row < u.N) ? t.v[c] : u32x4_t{0u, 0u, 0u, 0u};
+        }
+        bf16x8_t kf[2][KK];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) kf[mb][kk] = __builtin_bit_cast(bf16x8_t, t.k[mb][kk]);
+        f32x4_t s[NBW][2];
+        w.scores(kf, s);
+        if (k + 2 < nk) issue(t, k + 2);  // the registers are free again: keep two tiles in flight
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        bf16x8_t vf[DB];
+        const uint16_t* vrow = vlds + (size_t)(4 * quad + (r16 >> 2)) * VP + 4 * (r16 & 3);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const u32x2_t lo = lds_read_tr16(vrow + db * 16);
+            const u32x2_t hi = lds_read_tr16(vrow + 16 * VP + db * 16);
+            vf[db] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+        }
+        w.update(s, vf, t0, a.scale_log2, quad);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    TileRegs ta, tb;
+    if (nk > 0) issue(ta, 0);
+    if (nk > 1) issue(tb, 1);
+    for (int k = 0; k < nk; k += 2) {
+        consume(ta, k);
+        if (k + 1 < nk) consume(tb, k + 1);
+    }
+    finish_unit<D, NBW, WINDOWED>(a, u, w, wave, 0, WT, 1, reinterpret_cast<float*>(lds));
+}
+
+// ---------------------------------------------------------------------------------
+// LDS-shared main loop: WR row-waves share each tile (for R > 32), WT token groups.
+template <int D, int NBW, int CPW, bool WINDOWED>
+__global__ __launch_bounds__(512) void shared_kernel(const KernelArgs a) {
+    constexpr int KP = D + 8;  // padded pitch of the K tile
+    constexpr int VP = D + 8;  // padded pitch of the row-major V tile
+    constexpr int KT = T * KP;
+    constexpr int BUF = KT + T * VP;
+    constexpr int NCH = D / 8;  // 1-KiB chunks of a tile, K then V
+    constexpr int HALF = NCH / 2;
+    constexpr int KK = D / 32, DB = D / 16;
+
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int WR = a.row_waves, WT = a.token_groups;
+    const int tg = wave / WR, wr = wave - (wave / WR) * WR;
+    const int r16 = lane & 15, quad = lane >> 4;
+    uint16_t* tg_lds = lds + (size_t)tg * 2 * BUF;
+    const Unit u = decode_unit<WINDOWED>(a);
+    WaveRows<D, NBW, WINDOWED> w;
+    w.init(a, u, wr * NBW, lane);
+
+    const int32_t* pt_row = a.page_table + (size_t)u.b * a.stride;
+    const int last_page = (u.N - 1) / a.P;
+    const size_t head_elems = (size_t)a.P * D;
+    u32x4_t pre[CPW];
+
+    auto prefetch = [&](int tile) {
+        const int t0 = tile * T;
+        const int pid0 = clampi(pt_row[min(t0 / a.P, last_page)], 0, a.num_pages - 1);
+        const int pid1 = clampi(pt_row[min((t0 + 16) / a.P, last_page)], 0, a.num_pages - 1);
+        const size_t base0 = ((size_t)pid0 * a.Hkv + u.hk) * head_elems + (size_t)(t0 % a.P) * D;
+        const size_t base1 = ((size_t)pid1 * a.Hkv + u.hk) * head_elems + (size_t)((t0 + 16) % a.P) * D;
+#pragma unroll
+        for (int ci = 0; ci < CPW; ++ci) {
+            const int c = wr + ci * WR;
+            if (c < NCH) {
+                const bool is_v = c >= HALF;
+                const int cc = is_v ? c - HALF : c;
+                const int off = cc * 512 + lane * 8;
+                const int row = off / D, col = off - (off / D) * D;
+                const bool h1 = row >= 16;
+                pre[ci] = ldg16((is_v ? a.vc : a.kc) + (h1 ? base1 : base0) + (size_t)(row - (h1 ? 16 : 0)) * D + col);
+            }
+        }
+    };
+    auto store = [&](int tile, uint16_t* buf) {
+        const int t0 = tile * T;
+#pragma unroll
+        for (int ci = 0; ci < CPW; ++ci) {
+            const int c = wr + ci * WR;
+            if (c < NCH) {
+                const bool is_v = c >= HALF;
+                const int cc = is_v ? c - HALF : c;
+                const int off = cc * 512 + lane * 8;
+                const int row = off / D, col = off - (off / D) * D;
+                if (!is_v) *(u32x4_t*)(buf + row * KP + col) = pre[ci];
+                else *(u32x4_t*)(buf + KT + row * VP + col) = (t0 + row < u.N) ? pre[ci] : u32x4_t{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    auto compute = [&](int tile, const uint16_t* buf) {
+        bf16x8_t kf[2][KK];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                kf[mb][kk] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(buf + (mb * 16 + r16) * KP + kk * 32 + quad * 8));
+        f32x4_t s[NBW][2];
+        w.scores(kf, s);
+        bf16x8_t vf[DB];
+        const uint16_t* vrow = buf + KT + (size_t)(4 * quad + (r16 >> 2)) * VP + 4 * (r16 & 3);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const u32x2_t lo = lds_read_tr16(vrow + db * 16);
+            const u32x2_t hi = lds_read_tr16(vrow + 16 * VP + db * 16);
+            vf[db] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+        }
+        w.update(s, vf, tile * T, a.scale_log2, quad);
+    };
+
+    const int n_iter = u.uhi > u.ulo ? (u.uhi - u.ulo + WT - 1) / WT : 0;
+    int tile = u.ulo + tg;
+    if (n_iter > 0 && tile < u.uhi) prefetch(tile);
+    for (int it = 0; it < n_iter; ++it) {
+        uint16_t* buf = tg_lds + (it & 1) * BUF;
+        const bool valid = tile < u.uhi;
+        if (valid) store(tile, buf);
+        __syncthreads();
+        const int next = tile + WT;
+        if (next < u.uhi) prefetch(next);
+        if (valid) compute(tile, buf);
+        tile = next;
+    }
+    finish_unit<D, NBW, WINDOWED>(a, u, w, tg, wr, WT, WR, reinterpret_cast<float*>(lds));
+}
+
+// ---------------------------------------------------------------------------------
+// Separate combine (+ merge) of the splits: one workgroup per output row.
+template <int D>
+__global__ __launch_bounds__(256) void combine_kernel(const KernelArgs a) {
     constexpr int DL = D / 4;     // threads per split row, 4 floats each
     constexpr int SL = 256 / DL;  // splits reduced in parallel
     __shared__ float red_acc[SL][D];
     __shared__ float red_l[SL];
     __shared__ float red_m[4];
     __shared__ float o_c[D];
-    __shared__ float s_f[16];
+    __shared__ float s_f[kMaxFuture];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = blockIdx.x;
     const int pair = row / a.R, r = row - (row / a.R) * a.R;
     const int b = pair / a.Hkv, hk = pair - (pair / a.Hkv) * a.Hkv;
     const int u0 = a.pair_table[2 * pair], S = a.pair_table[2 * pair + 1];
+    if (S <= 1) return;  // a single split wrote its output itself
     const int i = r / a.g, l = r - (r / a.g) * a.g, h = hk * a.g + l;
     const size_t orow = (size_t)(b * a.K + i) * a.Hq + h;
 
@@ -338,9 +615,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
     if (M != kNegInf) {
         for (int s = sl; s < S; s += SL) {
             const size_t pr = (size_t)(u0 + s) * a.R + r;
-            const float w = fast_exp2(a.part_m[pr] - M);
-            acc += w * *(const f32x4_t*)(a.part_acc + pr * D + 4 * d4);
-            lsum += w * a.part_l[pr];
+            const float wgt = fast_exp2(a.part_m[pr] - M);
+            acc += wgt * *(const f32x4_t*)(a.part_acc + pr * D + 4 * d4);
+            lsum += wgt * a.part_l[pr];
         }
     }
     *(f32x4_t*)&red_acc[sl][4 * d4] = acc;
@@ -356,7 +633,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
     float lse = L > 0.f ? M + log2f(L) : kNegInf;
     __syncthreads();
 
-    if (MERGE) {
+    if (a.merge) {
         const int N = clampi(a.seq_lens[b], a.K, a.stride * a.P);
         const int p = N - a.K + i;
         const int f_hi = a.window_right < 0 ? N - 1 : min(N - 1, p + a.window_right);
@@ -389,8 +666,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
                 for (int f = 0; f < nf; ++f) {
                     const int j = p + 1 + f;
                     const int pid = clampi(pt_row[j / a.P], 0, a.num_pages - 1);
-                    const uint16_t* vrow = a.vc + (((size_t)pid * a.Hkv + hk) * a.P + (j % a.P)) * D;
-                    of += fast_exp2(s_f[f] - lse_f) * bf16_to_f32(vrow[tid]);
+                    of += fast_exp2(s_f[f] - lse_f) *
+                          bf16_to_f32(a.vc[(((size_t)pid * a.Hkv + hk) * a.P + (j % a.P)) * D + tid]);
                 }
                 o_c[tid] = o_c[tid] + wf * (of - o_c[tid]);
             }
@@ -398,35 +675,45 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
             __syncthreads();
         }
     }
-
     if (tid < D) a.out[orow * D + tid] = f32_to_bf16_rne(o_c[tid]);
     if (tid == 0 && a.lse) a.lse[orow] = lse;
 }
 
-template <int D, int NBW, int CPW, bool W>
-hipError_t launch_partial_t(const KernelShape& shape, int units, const PartialArgs& args, hipStream_t stream) {
-    auto fn = partial_kernel<D, NBW, CPW, W>;
-    static size_t attr_bytes = 0;  // largest dynamic LDS size granted so far
-    if (shape.lds_bytes > 65536 && shape.lds_bytes > attr_bytes) {
-        hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)shape.lds_bytes);
+template <typename F>
+hipError_t launch_with_lds(F fn, int units, int threads, size_t lds, const KernelArgs& args, hipStream_t stream,
+                           size_t* granted) {
+    if (lds > 65536 && lds > *granted) {
+        hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
-        attr_bytes = shape.lds_bytes;
+        *granted = lds;
     }
-    const int threads = 64 * shape.row_waves * shape.token_groups;
-    hipLaunchKernelGGL(fn, dim3(units), dim3(threads), shape.lds_bytes, stream, args);
+    hipLaunchKernelGGL(fn, dim3(units), dim3(threads), lds, stream, args);
     return hipGetLastError();
 }
 
+template <int D, int NBW, bool W>
+hipError_t launch_stream(const KernelShape& s, int units, const KernelArgs& args, hipStream_t stream) {
+    static size_t granted = 0;
+    return launch_with_lds(stream_kernel<D, NBW, W>, units, 64 * s.token_groups, s.lds_bytes, args, stream, &granted);
+}
+
+template <int D, int NBW, int CPW, bool W>
+hipError_t launch_shared(const KernelShape& s, int units, const KernelArgs& args, hipStream_t stream) {
+    static size_t granted = 0;
+    return launch_with_lds(shared_kernel<D, NBW, CPW, W>, units, 64 * s.row_waves * s.token_groups, s.lds_bytes,
+                           args, stream, &granted);
+}
+
 template <bool W>
-hipError_t dispatch_partial(const KernelShape& s, int units, const PartialArgs& args, hipStream_t stream) {
-#define BA_CASE(D_, NBW_, CPW_)                                                      \
-    if (s.head_dim == D_ && s.nbw == NBW_ && s.cpw == CPW_)                          \
-        return launch_partial_t<D_, NBW_, CPW_, W>(s, units, args, stream);
-    BA_CASE(64, 1, 4)
-    BA_CASE(64, 1, 8)
+hipError_t dispatch(const KernelShape& s, int units, const KernelArgs& args, hipStream_t stream) {
+    if (s.stream) {
+        if (s.head_dim == 64 && s.nbw == 1) return launch_stream<64, 1, W>(s, units, args, stream);
+        if (s.head_dim == 64 && s.nbw == 2) return launch_stream<64, 2, W>(s, units, args, stream);
+        return hipErrorInvalidValue;
+    }
+#define BA_CASE(D_, NBW_, CPW_) \
+    if (s.head_dim == D_ && s.nbw == NBW_ && s.cpw == CPW_) return launch_shared<D_, NBW_, CPW_, W>(s, units, args, stream);
     BA_CASE(64, 2, 4)
-    BA_CASE(64, 2, 8)
     BA_CASE(128, 1, 4)
     BA_CASE(128, 1, 8)
 #undef BA_CASE
@@ -435,29 +722,27 @@ hipError_t dispatch_partial(const KernelShape& s, int units, const PartialArgs& 
 
 }  // namespace
 
-size_t partial_lds_bytes(int head_dim, int nbw, int row_waves, int token_groups) {
-    const size_t buf = (size_t)kTileTokens * (head_dim + 8) + (size_t)head_dim * (kTileTokens + 8);
-    const size_t tiles = (size_t)token_groups * 2 * buf * sizeof(uint16_t);
-    const size_t merge = (size_t)token_groups * row_waves * nbw * 16 * (head_dim + 4) * sizeof(float);
-    return tiles > merge ? tiles : merge;
+size_t attention_lds_bytes(const KernelShape& s, int R) {
+    (void)R;
+    const int D = s.head_dim;
+    size_t loop;
+    if (s.stream)
+        loop = (size_t)s.token_groups * kTileTokens * (D + 8) * sizeof(uint16_t);
+    else
+        loop = (size_t)s.token_groups * 2 * ((size_t)kTileTokens * (D + 8) * 2) * sizeof(uint16_t);
+    const size_t epi = epilogue_floats(D, s.row_waves * s.nbw, s.token_groups) * sizeof(float);
+    return loop > epi ? loop : epi;
 }
 
-hipError_t launch_partial(const KernelShape& shape, bool windowed, int units, const PartialArgs& args,
-                          hipStream_t stream) {
-    return windowed ? dispatch_partial<true>(shape, units, args, stream)
-                    : dispatch_partial<false>(shape, units, args, stream);
+hipError_t launch_attention(const KernelShape& shape, bool windowed, int units, const KernelArgs& args,
+                            hipStream_t stream) {
+    return windowed ? dispatch<true>(shape, units, args, stream) : dispatch<false>(shape, units, args, stream);
 }
 
-hipError_t launch_combine(int head_dim, bool merge, int rows, const CombineArgs& args, hipStream_t stream) {
-    if (head_dim == 64) {
-        if (merge) hipLaunchKernelGGL((combine_kernel<64, true>), dim3(rows), dim3(256), 0, stream, args);
-        else hipLaunchKernelGGL((combine_kernel<64, false>), dim3(rows), dim3(256), 0, stream, args);
-    } else if (head_dim == 128) {
-        if (merge) hipLaunchKernelGGL((combine_kernel<128, true>), dim3(rows), dim3(256), 0, stream, args);
-        else hipLaunchKernelGGL((combine_kernel<128, false>), dim3(rows), dim3(256), 0, stream, args);
-    } else {
-        return hipErrorInvalidValue;
-    }
+hipError_t launch_combine(int head_dim, int rows, const KernelArgs& args, hipStream_t stream) {
+    if (head_dim == 64) hipLaunchKernelGGL(combine_kernel<64>, dim3(rows), dim3(256), 0, stream, args);
+    else if (head_dim == 128) hipLaunchKernelGGL(combine_kernel<128>, dim3(rows), dim3(256), 0, stream, args);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

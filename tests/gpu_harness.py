@@ -71,11 +71,18 @@ def run(dc: DeviceCase, *, window_left=None, window_right=None, splits=0, plan_l
     out = torch.empty(c.batch, c.block_size, c.num_q_heads, c.head_dim, dtype=torch.bfloat16, device=dc.q.device)
     lse = torch.empty(c.batch, c.block_size, c.num_q_heads, dtype=torch.float32, device=dc.q.device) \
         if (with_lse or prm.window_left != -1) else None
-    if prm.window_left == -1:
-        ba.blockattn_forward(plan, dc.q, dc.k, dc.v, dc.page_table, dc.seq_lens, ws, out, lse)
-    else:
-        ba.blockattn_windowed_forward(plan, dc.q, dc.k, dc.v, dc.page_table, dc.seq_lens, ws, out, lse)
+    fwd = ba.blockattn_forward if prm.window_left == -1 else ba.blockattn_windowed_forward
+    fwd(plan, dc.q, dc.k, dc.v, dc.page_table, dc.seq_lens, ws, out, lse)
     torch.cuda.synchronize()
+    # A second call on the same plan and workspace must give the same bits: the split
+    # counters of the fused combine reset themselves.
+    first = out.clone()
+    first_lse = lse.clone() if lse is not None else None
+    fwd(plan, dc.q, dc.k, dc.v, dc.page_table, dc.seq_lens, ws, out, lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out, first), "second call on the same plan differs"
+    if lse is not None:
+        assert torch.equal(lse, first_lse), "second call on the same plan differs (lse)"
     info = plan.info()
     if canary:
         assert bool((ws_all[nbytes:] == 0xA5).all()), "workspace guard bytes were overwritten"
