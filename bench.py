@@ -112,7 +112,7 @@ def load_traffic(case_name: str, per_launch_bytes: int):
     return rec.get("hbm_bytes_per_launch")
 
 
-def run_case(case, steps, warmup, threads, graph=True):
+def run_case(case, steps, warmup, threads, graph=True, splits=0, waves=0):
     import numpy as np
     import torch
 
@@ -141,7 +141,8 @@ def run_case(case, steps, warmup, threads, graph=True):
     prm = ba.make_params(batch=case.batch, block_size=case.block_size, num_q_heads=case.num_q_heads,
                          num_kv_heads=case.num_kv_heads, head_dim=case.head_dim, page_size=case.page_size,
                          page_table_stride=inp.page_table.shape[1], num_pages=inp.num_pages, sm_scale=case.scale,
-                         window_left=case.window_left, window_right=case.window_right)
+                         window_left=case.window_left, window_right=case.window_right, splits_override=splits,
+                         waves_override=waves)
     nbytes = ba.blockattn_workspace_size(prm, inp.seq_lens)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     plan = ba.blockattn_plan(prm, inp.seq_lens, ws, nbytes)
@@ -217,9 +218,33 @@ def run_case(case, steps, warmup, threads, graph=True):
         "units": info["units"],
         "max_splits": info["max_splits"],
         "waves_per_unit": info["waves_per_unit"],
+        "combine_launch": info["combine_launch"],
     }
     plan.destroy()
     return res, inp, out
+
+
+def stream_reference():
+    """Achievable read bandwidth: torch reductions over 2 GiB (8 rotating 256 MiB slices)."""
+    import torch
+
+    x = torch.ones(1 << 30, dtype=torch.bfloat16, device="cuda")
+    res = {}
+    for name, fn in (("sum_bf16", lambda t: t.sum(dtype=torch.float32)),
+                     ("amax_bf16", lambda t: t.amax())):
+        for _ in range(3):
+            fn(x)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(10):
+            fn(x)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / 10
+        res[name] = round(x.numel() * 2 / dt / 1e9, 1)
+    del x
+    torch.cuda.empty_cache()
+    log(f"[bench] streaming-read reference (GB/s): {res}")
+    return res
 
 
 def cpu_baseline(case, inp, gpu_out, kv_total, budget_s):
@@ -272,6 +297,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU budget of the oracle sample")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
+    ap.add_argument("--splits", type=int, default=0, help="force the split count per (request, kv head)")
+    ap.add_argument("--waves", type=int, default=0, help="force the tile-streaming waves per workgroup")
+    ap.add_argument("--stream-reference", action="store_true",
+                    help="also time plain streaming reads of 2 GiB (achievable HBM read bandwidth)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy 5 times (reference kernel for PMC byte counters)")
     args = ap.parse_args()
@@ -295,7 +324,8 @@ def main():
         log("[bench] copy calibration: 5 x 1 GiB device copies done")
 
     case = find_case(args.case)
-    res, inp, out = run_case(case, args.steps, args.warmup, threads, graph=not args.eager)
+    res, inp, out = run_case(case, args.steps, args.warmup, threads, graph=not args.eager, splits=args.splits,
+                             waves=args.waves)
     kvb = res["kv_bytes"]
     value = kvb / (res["step_ms"] * 1e-3) / 1e9
     achieved = kvb / (res["partial_ms"] * 1e-3) / 1e9
@@ -307,7 +337,8 @@ def main():
     if args.sweep:
         sweep = []
         for c in cases_for_config(case.cfg):
-            r, _, _ = run_case(c, max(10, args.steps // 2), 3, threads, graph=not args.eager)
+            r, _, _ = run_case(c, max(10, args.steps // 2), 3, threads, graph=not args.eager, splits=args.splits,
+                               waves=args.waves)
             r["gbs"] = r["kv_bytes"] / (r["step_ms"] * 1e-3) / 1e9
             r["frac"] = r["gbs"] / HBM_PEAK_GBS
             r["partial_gbs"] = r["kv_bytes"] / (r["partial_ms"] * 1e-3) / 1e9
@@ -317,6 +348,7 @@ def main():
                 f"{r['partial_gbs']:7.0f} GB/s  units {r['units']}")
             torch.cuda.empty_cache()
 
+    stream_ref = stream_reference() if args.stream_reference else None
     traffic = load_traffic(case.name, kvb)
     line = {
         "metric": METRIC,
@@ -347,6 +379,8 @@ def main():
                      "kernel_us": round(res["partial_ms"] * 1e3, 2), "kernel_events": res["kernel_timing"]},
         "cpu_baseline": None,
     }
+    if stream_ref is not None:
+        line["stream_reference"] = stream_ref
     if sweep is not None:
         line["sweep"] = [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()} for r in sweep]
     if not args.no_cpu_baseline:

@@ -80,6 +80,8 @@ typedef struct blockattn_params {
     int32_t splits_override;   /* 0: automatic split count. > 0: exactly that many KV splits per
                                   (request, kv head), clamped to the request's 32-token tile count
                                   (for testing split invariance and tuning) */
+    int32_t waves_override;    /* 0: automatic. > 0: tile-streaming wavefronts per workgroup (1..8),
+                                  reduced if the row-waves of a tile leave no room (tuning) */
 } blockattn_params;
 
 typedef struct blockattn_plan_s* blockattn_plan_t;
@@ -93,8 +95,8 @@ typedef struct blockattn_plan_info {
     int32_t token_groups;      /* wavefronts streaming different tiles inside one workgroup */
     int32_t row_waves;         /* wavefronts sharing one tile, each owning some query rows */
     int32_t uploaded;          /* 1 once the work list has been copied into a workspace */
-    int32_t fused_combine;     /* 1: the last split of a (request, kv head) combines inside the attention
-                                  kernel; 0: a separate combine launch follows (many splits) */
+    int32_t combine_launch;    /* 1: a combine kernel follows the attention kernel (some request has
+                                  more than one split); 0: every split wrote its output directly */
     size_t workspace_bytes;    /* bytes the plan needs */
 } blockattn_plan_info_t;
 

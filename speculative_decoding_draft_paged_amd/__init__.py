@@ -53,6 +53,7 @@ class blockattn_params(ctypes.Structure):
         ("window_right", ctypes.c_int32),
         ("sm_scale", ctypes.c_float),
         ("splits_override", ctypes.c_int32),
+        ("waves_override", ctypes.c_int32),
     ]
 
 
@@ -66,7 +67,7 @@ class blockattn_plan_info_t(ctypes.Structure):
         ("token_groups", ctypes.c_int32),
         ("row_waves", ctypes.c_int32),
         ("uploaded", ctypes.c_int32),
-        ("fused_combine", ctypes.c_int32),
+        ("combine_launch", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -123,9 +124,9 @@ def _check(status: int):
 
 
 def make_params(*, batch, block_size, num_q_heads, num_kv_heads, head_dim, page_size, page_table_stride, num_pages,
-                sm_scale, window_left=-1, window_right=-1, splits_override=0) -> blockattn_params:
+                sm_scale, window_left=-1, window_right=-1, splits_override=0, waves_override=0) -> blockattn_params:
     return blockattn_params(batch, block_size, num_q_heads, num_kv_heads, head_dim, page_size, page_table_stride,
-                            num_pages, window_left, window_right, float(sm_scale), splits_override)
+                            num_pages, window_left, window_right, float(sm_scale), splits_override, waves_override)
 
 
 def _host_lens(seq_lens_host):

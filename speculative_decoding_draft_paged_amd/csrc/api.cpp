@@ -44,12 +44,10 @@ constexpr int kMaxWavesPerCU = 8;  // two waves per SIMD at ~200 VGPRs
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Layout {
-    size_t work = 0, pairs = 0, counters = 0, m = 0, l = 0, acc = 0, total = 0;
+    size_t work = 0, pairs = 0, m = 0, l = 0, acc = 0, total = 0;
 };
 
-// The last unit to finish combines its request's splits when there are at most this
-// many; beyond it a separate combine launch spreads the work over one workgroup per row.
-constexpr int kFuseMaxSplits = 16;
+
 
 }  // namespace
 
@@ -59,8 +57,8 @@ struct blockattn_plan_s {
     int g = 1, R = 1, NB = 1;
     KernelShape shape{};
     bool merge_active = false;
-    bool fused = true;
     int units = 0, max_splits = 0;
+    int uniform_splits = 0;  // > 0 when every (request, kv head) has this split count
     std::vector<WorkItem> work;
     std::vector<int32_t> pair_table;
     Layout lay;
@@ -101,6 +99,8 @@ int validate(const blockattn_params* p, const int32_t* lens) {
         return fail(BLOCKATTN_ERR_INVALID_ARGUMENT,
                     "window_right must be -1 for the unwindowed form (window_left = -1)");
     if (p->splits_override < 0) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "splits_override must be >= 0");
+    if (p->waves_override < 0 || p->waves_override > kMaxWaves)
+        return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "waves_override must be in [0, 8]");
     const long max_keys = (long)p->page_table_stride * p->page_size;
     if (max_keys > (1L << 30))
         return fail(BLOCKATTN_ERR_UNSUPPORTED, "page_table_stride * page_size must be <= 2^30 keys");
@@ -129,7 +129,7 @@ int tiles_for(const blockattn_params* p, int n) {
     return (n + kTileTokens - 1) / kTileTokens - lo / kTileTokens;
 }
 
-KernelShape choose_shape(int D, int NB, int R) {
+KernelShape choose_shape(int D, int NB, int R, int waves_override) {
     KernelShape s{};
     s.head_dim = D;
     if (D == 64 && NB <= 2) {
@@ -151,6 +151,7 @@ KernelShape choose_shape(int D, int NB, int R) {
         const int need = (nch + s.row_waves - 1) / s.row_waves;
         s.cpw = need <= 4 ? 4 : 8;
     }
+    if (waves_override > 0) s.token_groups = std::max(1, std::min(waves_override, kMaxWaves / s.row_waves));
     s.lds_bytes = attention_lds_bytes(s, R);
     while (s.lds_bytes > kLdsPerCU && s.token_groups > 1) {
         --s.token_groups;
@@ -167,7 +168,7 @@ int build_plan(const blockattn_params* p, const int32_t* lens, blockattn_plan_s*
     pl->g = p->num_q_heads / p->num_kv_heads;
     pl->R = p->block_size * pl->g;
     pl->NB = (pl->R + 15) / 16;
-    pl->shape = choose_shape(p->head_dim, pl->NB, pl->R);
+    pl->shape = choose_shape(p->head_dim, pl->NB, pl->R, p->waves_override);
     pl->merge_active = pl->kind == 1 && p->block_size > 1 && p->window_right != 0;
 
     const int B = p->batch, H = p->num_kv_heads;
@@ -204,13 +205,14 @@ int build_plan(const blockattn_params* p, const int32_t* lens, blockattn_plan_s*
     if (pl->work.size() > 0x7FFFFFFFu / 2)
         return fail(BLOCKATTN_ERR_UNSUPPORTED, "too many work units; lower batch or splits_override");
     pl->units = (int)pl->work.size();
-    pl->fused = pl->max_splits <= kFuseMaxSplits;
+    pl->uniform_splits = pl->max_splits;
+    for (size_t pr = 0; pr < (size_t)B * H; ++pr)
+        if (pl->pair_table[2 * pr + 1] != pl->max_splits) pl->uniform_splits = 0;
 
     Layout& L = pl->lay;
     L.work = 0;
     L.pairs = align_up(L.work + pl->work.size() * sizeof(WorkItem), 256);
-    L.counters = align_up(L.pairs + pl->pair_table.size() * sizeof(int32_t), 256);
-    L.m = align_up(L.counters + (size_t)B * H * sizeof(int32_t), 256);
+    L.m = align_up(L.pairs + pl->pair_table.size() * sizeof(int32_t), 256);
     L.l = align_up(L.m + (size_t)pl->units * pl->R * sizeof(float), 256);
     L.acc = align_up(L.l + (size_t)pl->units * pl->R * sizeof(float), 256);
     L.total = align_up(L.acc + (size_t)pl->units * pl->R * p->head_dim * sizeof(float), 256);
@@ -249,7 +251,6 @@ int run_forward(blockattn_plan_t plan, const void* q, const void* k, const void*
     ka.seq_lens = lens;
     ka.work = reinterpret_cast<const WorkItem*>(base + plan->lay.work);
     ka.pair_table = reinterpret_cast<const int32_t*>(base + plan->lay.pairs);
-    ka.counters = reinterpret_cast<int32_t*>(base + plan->lay.counters);
     ka.part_m = reinterpret_cast<float*>(base + plan->lay.m);
     ka.part_l = reinterpret_cast<float*>(base + plan->lay.l);
     ka.part_acc = reinterpret_cast<float*>(base + plan->lay.acc);
@@ -267,7 +268,7 @@ int run_forward(blockattn_plan_t plan, const void* q, const void* k, const void*
     ka.window_right = p.window_right;
     ka.row_waves = plan->shape.row_waves;
     ka.token_groups = plan->shape.token_groups;
-    ka.fused = plan->fused ? 1 : 0;
+    ka.uniform_splits = plan->uniform_splits;
     ka.merge = plan->merge_active ? 1 : 0;
     ka.scale_log2 = (float)((double)p.sm_scale * 1.4426950408889634);
 
@@ -276,7 +277,7 @@ int run_forward(blockattn_plan_t plan, const void* q, const void* k, const void*
     if (e == hipSuccess) e = launch_attention(plan->shape, plan->kind == 1, plan->units, ka, st);
     if (e == hipSuccess && plan->prof_after) e = hipEventRecord(plan->prof_after, st);
     if (e != hipSuccess) return fail(BLOCKATTN_ERR_HIP, std::string("attention kernel launch: ") + hipGetErrorString(e));
-    if (!plan->fused && plan->max_splits > 1) {
+    if (plan->max_splits > 1) {
         const int rows = p.batch * p.num_kv_heads * plan->R;
         e = launch_combine(p.head_dim, rows, ka, st);
         if (e != hipSuccess)
@@ -318,7 +319,7 @@ int blockattn_plan(const blockattn_params* params, const int32_t* seq_lens_host,
             delete pl;
             return fail(BLOCKATTN_ERR_WORKSPACE_TOO_SMALL, buf);
         }
-        const size_t head = pl->lay.m;  // work list, pair table and zeroed split counters
+        const size_t head = pl->lay.m;  // work list and pair table
         hipError_t e = hipHostMalloc(&pl->stage, head, hipHostMallocDefault);
         if (e != hipSuccess) {
             delete pl;
@@ -370,7 +371,7 @@ int blockattn_plan_info(blockattn_plan_t plan, blockattn_plan_info_t* info) {
     info->token_groups = plan->shape.token_groups;
     info->row_waves = plan->shape.row_waves;
     info->uploaded = plan->uploaded ? 1 : 0;
-    info->fused_combine = plan->fused ? 1 : 0;
+    info->combine_launch = plan->max_splits > 1 ? 1 : 0;
     info->workspace_bytes = plan->lay.total;
     return BLOCKATTN_OK;
 }

@@ -10,6 +10,7 @@ constexpr int kTileTokens = 32;   // keys per tile: one MFMA K-step of PV, two 1
 constexpr int kMaxRowBlocks = 8;  // R = K * group <= 128 query rows per kv head
 constexpr int kMaxWaves = 8;      // wavefronts per workgroup of the attention kernel
 constexpr int kMaxFuture = 16;    // future block keys per row the merge can hold (K <= 16)
+constexpr int kPidWindow = 2048;     // tiles whose page ids the streaming kernel stages in LDS at a time
 
 // One unit of split-KV work. Tiles [lo, hi) of the key range of (b, h_kv) are derived on
 // the device from the live sequence length: unit s of S covers tiles tb + s*nt/S ..
@@ -26,7 +27,6 @@ struct KernelArgs {
     const int32_t* seq_lens;
     const WorkItem* work;
     const int32_t* pair_table;  // per (b, h_kv): first unit, split count
-    int32_t* counters;          // per (b, h_kv): units finished (the last one resets it to 0)
     float* part_m;
     float* part_l;
     float* part_acc;
@@ -37,7 +37,7 @@ struct KernelArgs {
     int32_t window_right;  // -1: every later block key
     int32_t row_waves;     // WR: waves sharing a tile, each owning NBW row blocks (shared loop only)
     int32_t token_groups;  // WT: tile streams per workgroup
-    int32_t fused;         // 1: the last unit of a (b, h_kv) combines the splits; 0: a combine kernel does
+    int32_t uniform_splits;  // > 0: every (b, h_kv) has this many splits, unit = pair * S + s (no work list read)
     int32_t merge;         // 1: fold in the block keys after each query (windowed form)
     float scale_log2;      // sm_scale * log2(e)
 };

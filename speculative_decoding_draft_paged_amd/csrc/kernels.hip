@@ -1,6 +1,6 @@
 // gfx950 kernels for draft-block paged attention.
 //
-// attention kernels (split-KV partial attention with a fused epilogue). One
+// attention kernels (split-KV partial attention and its epilogue). One
 // workgroup = one work unit: a range of 32-token key tiles of one (request b,
 // kv head). Per tile:
 //   - S^T = K Q^T on v_mfma_f32_16x16x32_bf16. Tokens are the M dimension and
@@ -21,17 +21,17 @@
 //   shared_kernel (large R): WR row-waves share each tile through a double-
 //     buffered LDS copy and own some 16-row blocks each.
 // Epilogue: the token groups of the workgroup merge through LDS. A unit that is
-// its request's only split writes the final bf16 output and base-2 LSE itself.
-// Otherwise it writes its fp32 (acc, m, l); with the fused combine the last
-// unit of the (request, kv head) to finish (an agent-scope counter) combines
-// all splits and writes the result. The windowed form then folds in the block
-// keys after each query by the LSE merge (TensorRT-LLM PR #21130, Description
-// item 1 and its formulation table: lse = lse_c (+) lse_f, out = out_c +
-// w (out_f - out_c), w = 2^(lse_f - lse)).
+// its request's only split writes the final bf16 output and base-2 LSE itself,
+// and for the windowed form folds in the block keys after each query by the LSE
+// merge (TensorRT-LLM PR #21130, Description item 1 and its formulation table:
+// lse = lse_c (+) lse_f, out = out_c + w (out_f - out_c), w = 2^(lse_f - lse)).
+// Otherwise it writes its fp32 (acc, m, l) partial.
 //
-// combine_kernel: the same combine and merge as a separate launch, one
-// workgroup per output row, for plans with many splits per request (small batch,
-// long context), where one workgroup per request would serialise the combine.
+// combine_kernel: the LSE combine of the splits and the same merge, one workgroup
+// per output row, launched after the attention kernel. (Combining inside the
+// attention kernel by its last-finishing unit needs an agent-scope release and
+// acquire per unit; on this part those cache write-backs cost far more than a
+// second launch.)
 //
 // The split-KV form itself follows the flash-decoding rework of TensorRT-LLM
 // PR #16150 (paged DFlash cross-attention, commits "rework flash-decoding style"
@@ -83,7 +83,16 @@ struct Unit {
 
 template <bool WINDOWED>
 __device__ __forceinline__ Unit decode_unit(const KernelArgs& a) {
-    const WorkItem wi = a.work[blockIdx.x];
+    WorkItem wi;
+    if (a.uniform_splits > 0) {  // every (request, kv head) has the same split count: no work-list load
+        const int pair = blockIdx.x / a.uniform_splits;
+        wi.b = pair / a.Hkv;
+        wi.hk = pair - wi.b * a.Hkv;
+        wi.s = blockIdx.x - pair * a.uniform_splits;
+        wi.S = a.uniform_splits;
+    } else {
+        wi = a.work[blockIdx.x];
+    }
     Unit u;
     u.b = wi.b;
     u.hk = wi.hk;
@@ -99,7 +108,8 @@ __device__ __forceinline__ Unit decode_unit(const KernelArgs& a) {
 }
 
 // Per-wave query fragments (B operand of S^T = K Q^T), row key bounds and softmax state.
-template <int D, int NBW, bool WINDOWED>
+// ALL_ON: every owned 16-row block holds live rows (no per-block skip test).
+template <int D, int NBW, bool WINDOWED, bool ALL_ON = false>
 struct WaveRows {
     static constexpr int KK = D / 32, DB = D / 16;
     bf16x8_t qf[NBW][KK];
@@ -144,7 +154,7 @@ struct WaveRows {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) {
                 s[n][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                if (on[n]) {
+                if (ALL_ON || on[n]) {
 #pragma unroll
                     for (int kk = 0; kk < KK; ++kk)
                         s[n][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mb][kk], qf[n][kk], s[n][mb], 0, 0, 0);
@@ -159,7 +169,7 @@ struct WaveRows {
         const bool edge = (t0 < lo_max) || (t0 + T - 1 > hi_min);
 #pragma unroll
         for (int n = 0; n < NBW; ++n) {
-            if (!on[n]) continue;
+            if (!ALL_ON && !on[n]) continue;
             float x[8];
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
@@ -203,13 +213,13 @@ struct WaveRows {
 
 // Floats of LDS the epilogue needs (it reuses the tile buffers).
 __host__ __device__ constexpr size_t epilogue_floats(int D, int slots_per_group, int token_groups) {
-    return (size_t)token_groups * slots_per_group * 16 * (D + 4) + 2 * 128 + 128 * kMaxFuture + 4;
+    return (size_t)token_groups * slots_per_group * 16 * (D + 4) + 2 * 128 + 128 * kMaxFuture;
 }
 
 // Merge the wave states of a workgroup, then write a partial, or (only split /
 // last arriver) the final bf16 output and LSE, with the windowed merge.
-template <int D, int NBW, bool WINDOWED>
-__device__ void finish_unit(const KernelArgs& a, const Unit& u, WaveRows<D, NBW, WINDOWED>& w, int tg, int wr,
+template <int D, int NBW, bool WINDOWED, bool ALL_ON>
+__device__ void finish_unit(const KernelArgs& a, const Unit& u, WaveRows<D, NBW, WINDOWED, ALL_ON>& w, int tg, int wr,
                             int WT, int WR, float* lds) {
     constexpr int DB = D / 16, MP = D + 4;
     const int tid = threadIdx.x, nthreads = blockDim.x;
@@ -220,7 +230,6 @@ __device__ void finish_unit(const KernelArgs& a, const Unit& u, WaveRows<D, NBW,
     float* rowM = mg + (size_t)WT * slots * 16 * MP;
     float* rowL = rowM + 128;
     float* sf = rowL + 128;
-    int* flag = reinterpret_cast<int*>(sf + 128 * kMaxFuture);
 
 #pragma unroll
     for (int n = 0; n < NBW; ++n) {
@@ -265,7 +274,6 @@ __device__ void finish_unit(const KernelArgs& a, const Unit& u, WaveRows<D, NBW,
         __syncthreads();
     }
 
-    const int pair = u.b * a.Hkv + u.hk;
     if (u.S > 1) {
         const size_t row0 = (size_t)blockIdx.x * R;
         for (int idx = tid; idx < R * (D / 4); idx += nthreads) {
@@ -276,50 +284,13 @@ __device__ void finish_unit(const KernelArgs& a, const Unit& u, WaveRows<D, NBW,
             a.part_m[row0 + r] = rowM[r];
             a.part_l[row0 + r] = rowL[r];
         }
-        if (!a.fused) return;
-        // Publish this unit's partial at agent scope, then count it. The unit that
-        // brings the count to S combines; it also resets the counter for the next call.
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __syncthreads();
-        if (tid == 0) {
-            const int prev = __hip_atomic_fetch_add(a.counters + pair, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-            const int last = prev == u.S - 1;
-            if (last) __hip_atomic_store(a.counters + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            *flag = last;
-        }
-        __syncthreads();
-        if (!*flag) return;
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        const int u0 = a.pair_table[2 * pair];
-        for (int r = tid; r < R; r += nthreads) {
-            float M = kNegInf;
-            for (int s = 0; s < u.S; ++s) M = fmaxf(M, a.part_m[(size_t)(u0 + s) * R + r]);
-            float L = 0.f;
-            if (M != kNegInf)
-                for (int s = 0; s < u.S; ++s)
-                    L += fast_exp2(a.part_m[(size_t)(u0 + s) * R + r] - M) * a.part_l[(size_t)(u0 + s) * R + r];
-            rowM[r] = M;
-            rowL[r] = L;
-        }
-        __syncthreads();
-        for (int idx = tid; idx < R * (D / 4); idx += nthreads) {
-            const int r = idx / (D / 4), d4 = idx - (idx / (D / 4)) * (D / 4);
-            const float M = rowM[r];
-            f32x4_t A = {0.f, 0.f, 0.f, 0.f};
-            if (M != kNegInf)
-                for (int s = 0; s < u.S; ++s) {
-                    const size_t pr = (size_t)(u0 + s) * R + r;
-                    A += fast_exp2(a.part_m[pr] - M) * *(const f32x4_t*)(a.part_acc + pr * D + 4 * d4);
-                }
-            *(f32x4_t*)(mg + (size_t)r * MP + 4 * d4) = A;
-        }
-        __syncthreads();
+        return;  // the combine kernel finishes this (request, kv head)
     }
 
     // Final stage: out = acc / L, lse = M + log2 L, then the future-block-key merge.
     const int32_t* pt_row = a.page_table + (size_t)u.b * a.stride;
     if (a.merge) {
-        const int nw = nthreads >> 6, wv = tid >> 6;
+        const int nw = nthreads >> 6, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
         for (int r = wv; r < R; r += nw) {
             const int i = r / a.g, h = u.hk * a.g + (r - (r / a.g) * a.g);
             const int p = u.C + i;
@@ -376,112 +347,133 @@ __device__ void finish_unit(const KernelArgs& a, const Unit& u, WaveRows<D, NBW,
 // ---------------------------------------------------------------------------------
 // Streaming main loop: one wave owns every row (R <= 16 * NBW), WT waves per
 // workgroup stream interleaved tiles of the unit, two tiles in flight per wave.
+// The page ids of up to kPidWindow tiles are staged in LDS by the whole workgroup
+// (one gather round trip), so the tile loads depend only on short LDS reads. Every
+// global load of the loop sits at a fixed, unconditional place (tile indices past
+// the wave's last tile are clamped to it), which keeps the compiler's wait counts
+// exact: the wait for one tile never drains the tile behind it.
 template <int D, int NBW, bool WINDOWED>
 __global__ __launch_bounds__(512) void stream_kernel(const KernelArgs a) {
     constexpr int KK = D / 32, DB = D / 16;
-    constexpr int VCH = D / 16;  // 1-KiB chunks of the V tile (16 bytes per lane each)
-    constexpr int VP = D + 8;    // padded row pitch of the V tile in LDS (bf16 elements)
-    constexpr int RPC = 512 / D; // tile rows per chunk
+    constexpr int VCH = D / 16;   // 1-KiB chunks of the V tile (16 bytes per lane each)
+    constexpr int VP = D + 8;     // padded row pitch of the V tile in LDS (bf16 elements)
+    constexpr int RPC = 512 / D;  // tile rows per chunk
 
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x, nthreads = blockDim.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
     const int r16 = lane & 15, quad = lane >> 4;
     const int WT = a.token_groups;
     const Unit u = decode_unit<WINDOWED>(a);
-    WaveRows<D, NBW, WINDOWED> w;
+    WaveRows<D, NBW, WINDOWED, true> w;
     w.init(a, u, 0, lane);
     uint16_t* vlds = lds + (size_t)wave * T * VP;
+    int* pid_tab = reinterpret_cast<int*>(lds + (size_t)WT * T * VP);
 
-    const int span = u.uhi - u.ulo;
-    const int nk = span > wave ? (span - wave + WT - 1) / WT : 0;
     const int32_t* pt_row = a.page_table + (size_t)u.b * a.stride;
     const int last_page = (u.N - 1) / a.P;
     const size_t head_elems = (size_t)a.P * D;
-
-    // Page ids of the wave's tiles kb .. kb+31 (lane 2j + h: half h of tile kb + j),
-    // and of the 32 tiles after them.
-    auto load_pids = [&](int kbase) {
-        const int k = kbase + (lane >> 1);
-        if (k >= nk) return 0;
-        const int tok = (u.ulo + wave + k * WT) * T + 16 * (lane & 1);
-        return clampi(pt_row[min(tok / a.P, last_page)], 0, a.num_pages - 1);
-    };
-    int kb = 0;
-    int pid_cur = load_pids(0);
-    int pid_nxt = load_pids(32);
 
     struct TileRegs {
         u32x4_t k[2][KK];
         u32x4_t v[VCH];
     };
-    auto issue = [&](TileRegs& t, int k) {
-        const int j = 2 * (k - kb);
-        const int pid0 = j < 64 ? __builtin_amdgcn_readlane(pid_cur, j) : __builtin_amdgcn_readlane(pid_nxt, j - 64);
-        const int pid1 = j < 64 ? __builtin_amdgcn_readlane(pid_cur, j + 1)
-                                : __builtin_amdgcn_readlane(pid_nxt, j - 63);
-        const int t0 = (u.ulo + wave + k * WT) * T;
-        const size_t base0 = ((size_t)pid0 * a.Hkv + u.hk) * head_elems + (size_t)(t0 % a.P) * D;
-        const size_t base1 = ((size_t)pid1 * a.Hkv + u.hk) * head_elems + (size_t)((t0 + 16) % a.P) * D;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-                t.k[mb][kk] = ldg16(a.kc + (mb ? base1 : base0) + (size_t)r16 * D + kk * 32 + quad * 8);
-#pragma unroll
-        for (int c = 0; c < VCH; ++c) {
-            const int row = c * RPC + (lane * 8) / D;  // tile row of this lane's 16 bytes
-            const int col = (lane * 8) % D;
-            const bool h1 = c * RPC >= 16;
-            t.v[c] = ldg16(a.vc + (h1 ? base1 : base0) + (size_t)(row - (h1 ? 16 : 0)) * D + col);
-        }
-    };
 
-    auto consume = [&](TileRegs& t, int k) {
-        if (k - kb == 32) {  // slide the page-id window
-            kb += 32;
-            pid_cur = pid_nxt;
-            pid_nxt = load_pids(kb + 32);
+    for (int win = u.ulo; win < u.uhi; win += kPidWindow) {
+        const int span = min(u.uhi - win, kPidWindow);
+        __syncthreads();  // the previous window is done with the page-id table
+        {
+            // entry 2j + h: page of half h (16 tokens) of tile win + j
+            const int n = 2 * span;
+            for (int j0 = 0; j0 < n; j0 += 8 * nthreads) {
+                int v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int j = j0 + e * nthreads + tid;
+                    const int tok = (win + (j >> 1)) * T + 16 * (j & 1);
+                    v[e] = j < n ? pt_row[min(tok / a.P, last_page)] : 0;
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int j = j0 + e * nthreads + tid;
+                    if (j < n) pid_tab[j] = clampi(v[e], 0, a.num_pages - 1);
+                }
+            }
         }
-        const int t0 = (u.ulo + wave + k * WT) * T;
-#pragma unroll
-        for (int c = 0; c < VCH; ++c) {
-            const int row = c * RPC + (lane * 8) / D;
-            const int col = (lane * 8) % D;
-            *(u32x4_t*)(vlds + row * VP + col) = (t0 + row < u.N) ? t.v[c] : u32x4_t{0u, 0u, 0u, 0u};
-        }
-        bf16x8_t kf[2][KK];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) kf[mb][kk] = __builtin_bit_cast(bf16x8_t, t.k[mb][kk]);
-        f32x4_t s[NBW][2];
-        w.scores(kf, s);
-        if (k + 2 < nk) issue(t, k + 2);  // the registers are free again: keep two tiles in flight
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        bf16x8_t vf[DB];
-        const uint16_t* vrow = vlds + (size_t)(4 * quad + (r16 >> 2)) * VP + 4 * (r16 & 3);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const u32x2_t lo = lds_read_tr16(vrow + db * 16);
-            const u32x2_t hi = lds_read_tr16(vrow + 16 * VP + db * 16);
-            vf[db] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
-        }
-        w.update(s, vf, t0, a.scale_log2, quad);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
+        __syncthreads();
+        const int nk = span > wave ? (span - wave + WT - 1) / WT : 0;
+        if (nk == 0) continue;
 
-    TileRegs ta, tb;
-    if (nk > 0) issue(ta, 0);
-    if (nk > 1) issue(tb, 1);
-    for (int k = 0; k < nk; k += 2) {
-        consume(ta, k);
-        if (k + 1 < nk) consume(tb, k + 1);
+        auto issue = [&](TileRegs& t, int k) {
+            const int kc = min(k, nk - 1);
+            const int j = 2 * (wave + kc * WT);
+            const int pid0 = pid_tab[j], pid1 = pid_tab[j + 1];
+            const int t0 = (win + wave + kc * WT) * T;
+            const size_t base0 = ((size_t)pid0 * a.Hkv + u.hk) * head_elems + (size_t)(t0 % a.P) * D;
+            const size_t base1 = ((size_t)pid1 * a.Hkv + u.hk) * head_elems + (size_t)((t0 + 16) % a.P) * D;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk)
+                    t.k[mb][kk] = ldg16(a.kc + (mb ? base1 : base0) + (size_t)r16 * D + kk * 32 + quad * 8);
+#pragma unroll
+            for (int c = 0; c < VCH; ++c) {
+                const int row = c * RPC + (lane * 8) / D;  // tile row of this lane's 16 bytes
+                const int col = (lane * 8) % D;
+                const bool h1 = c * RPC >= 16;
+                t.v[c] = ldg16(a.vc + (h1 ? base1 : base0) + (size_t)(row - (h1 ? 16 : 0)) * D + col);
+            }
+        };
+
+        auto consume = [&](TileRegs& t, int k, bool valid, bool reissue) {
+            const int t0 = (win + wave + k * WT) * T;
+            f32x4_t s[NBW][2];
+            if (valid) {
+#pragma unroll
+                for (int c = 0; c < VCH; ++c) {
+                    const int row = c * RPC + (lane * 8) / D;
+                    const int col = (lane * 8) % D;
+                    *(u32x4_t*)(vlds + row * VP + col) = (t0 + row < u.N) ? t.v[c] : u32x4_t{0u, 0u, 0u, 0u};
+                }
+                bf16x8_t kf[2][KK];
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int kk = 0; kk < KK; ++kk) kf[mb][kk] = __builtin_bit_cast(bf16x8_t, t.k[mb][kk]);
+                w.scores(kf, s);
+            }
+            if (reissue) issue(t, k + 2);  // the registers are free again: keep two tiles in flight
+            if (valid) {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                bf16x8_t vf[DB];
+                const uint16_t* vrow = vlds + (size_t)(4 * quad + (r16 >> 2)) * VP + 4 * (r16 & 3);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const u32x2_t lo = lds_read_tr16(vrow + db * 16);
+                    const u32x2_t hi = lds_read_tr16(vrow + 16 * VP + db * 16);
+                    vf[db] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+                }
+                w.update(s, vf, t0, a.scale_log2, quad);
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
+        };
+
+        // Tile A's loads come first on every path into the loop head and tile B's right
+        // after, so each wait below names exactly one tile.
+        TileRegs ta, tb;
+        issue(ta, 0);
+        for (int k = 0; k < nk; k += 2) {
+            issue(tb, k + 1);
+            consume(ta, k, true, true);
+            consume(tb, k + 1, k + 1 < nk, false);
+        }
     }
-    finish_unit<D, NBW, WINDOWED>(a, u, w, wave, 0, WT, 1, reinterpret_cast<float*>(lds));
+    finish_unit(a, u, w, wave, 0, WT, 1, reinterpret_cast<float*>(lds));
 }
 
 // ---------------------------------------------------------------------------------
@@ -497,7 +489,8 @@ __global__ __launch_bounds__(512) void shared_kernel(const KernelArgs a) {
     constexpr int KK = D / 32, DB = D / 16;
 
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar) index
     const int WR = a.row_waves, WT = a.token_groups;
     const int tg = wave / WR, wr = wave - (wave / WR) * WR;
     const int r16 = lane & 15, quad = lane >> 4;
@@ -578,7 +571,7 @@ __global__ __launch_bounds__(512) void shared_kernel(const KernelArgs a) {
         if (valid) compute(tile, buf);
         tile = next;
     }
-    finish_unit<D, NBW, WINDOWED>(a, u, w, tg, wr, WT, WR, reinterpret_cast<float*>(lds));
+    finish_unit(a, u, w, tg, wr, WT, WR, reinterpret_cast<float*>(lds));
 }
 
 // ---------------------------------------------------------------------------------
@@ -603,6 +596,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const KernelArgs a) {
     const size_t orow = (size_t)(b * a.K + i) * a.Hq + h;
 
     float mloc = kNegInf;
+#pragma unroll 2
     for (int s = tid; s < S; s += 256) mloc = fmaxf(mloc, a.part_m[(size_t)(u0 + s) * a.R + r]);
     for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
     if (lane == 0) red_m[wave] = mloc;
@@ -613,6 +607,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const KernelArgs a) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     float lsum = 0.f;
     if (M != kNegInf) {
+#pragma unroll 4
         for (int s = sl; s < S; s += SL) {
             const size_t pr = (size_t)(u0 + s) * a.R + r;
             const float wgt = fast_exp2(a.part_m[pr] - M);
@@ -727,7 +722,7 @@ size_t attention_lds_bytes(const KernelShape& s, int R) {
     const int D = s.head_dim;
     size_t loop;
     if (s.stream)
-        loop = (size_t)s.token_groups * kTileTokens * (D + 8) * sizeof(uint16_t);
+        loop = (size_t)s.token_groups * kTileTokens * (D + 8) * sizeof(uint16_t) + 2 * kPidWindow * sizeof(int);
     else
         loop = (size_t)s.token_groups * 2 * ((size_t)kTileTokens * (D + 8) * 2) * sizeof(uint16_t);
     const size_t epi = epilogue_floats(D, s.row_waves * s.nbw, s.token_groups) * sizeof(float);

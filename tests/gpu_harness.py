@@ -44,7 +44,7 @@ def upload(inputs: synth.Inputs, device="cuda") -> DeviceCase:
                       torch.from_numpy(np.ascontiguousarray(inputs.seq_lens)).to(device))
 
 
-def params_for(dc: DeviceCase, *, window_left=None, window_right=None, splits=0, scale=None):
+def params_for(dc: DeviceCase, *, window_left=None, window_right=None, splits=0, scale=None, waves=0):
     c = dc.inputs.case
     return ba.make_params(batch=c.batch, block_size=c.block_size, num_q_heads=c.num_q_heads,
                           num_kv_heads=c.num_kv_heads, head_dim=c.head_dim, page_size=c.page_size,
@@ -52,14 +52,14 @@ def params_for(dc: DeviceCase, *, window_left=None, window_right=None, splits=0,
                           sm_scale=c.scale if scale is None else scale,
                           window_left=c.window_left if window_left is None else window_left,
                           window_right=c.window_right if window_right is None else window_right,
-                          splits_override=splits)
+                          splits_override=splits, waves_override=waves)
 
 
 def run(dc: DeviceCase, *, window_left=None, window_right=None, splits=0, plan_lens=None, with_lse=True,
-        canary=False):
+        canary=False, waves=0):
     """Plan + forward on the current stream; returns (out float32 np, lse np or None, info)."""
     c = dc.inputs.case
-    prm = params_for(dc, window_left=window_left, window_right=window_right, splits=splits)
+    prm = params_for(dc, window_left=window_left, window_right=window_right, splits=splits, waves=waves)
     lens = dc.inputs.seq_lens if plan_lens is None else plan_lens
     nbytes = ba.blockattn_workspace_size(prm, lens)
     guard = 4096 if canary else 0

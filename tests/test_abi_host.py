@@ -25,8 +25,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layouts_match_header():
-    # params: 11 int32 + 1 float = 48 bytes; info: 9 int32 + padding + size_t
-    assert ctypes.sizeof(ba.blockattn_params) == 48
+    # params: 12 int32 + 1 float = 52 bytes; info: 9 int32 + padding + size_t
+    assert ctypes.sizeof(ba.blockattn_params) == 52
     assert ctypes.sizeof(ba.blockattn_plan_info_t) == 48
 
 
@@ -60,6 +60,14 @@ def test_split_heuristic_fills_the_gpu_and_bounds_partials():
     # every split keeps >= R/4 tiles of keys
     tiny = plan_info(params(batch=1), [200])
     assert tiny["max_splits"] == 1
+
+
+def test_waves_override():
+    assert plan_info(params(waves_override=8), [5000, 5000])["token_groups"] == 8
+    assert plan_info(params(waves_override=1), [5000, 5000])["waves_per_unit"] == 1
+    w = dict(head_dim=128, page_size=64, num_q_heads=16, num_kv_heads=1, window_left=4096, block_size=7)
+    info = plan_info(params(**w, waves_override=8), [8199, 8199])
+    assert info["row_waves"] == 7 and info["token_groups"] == 1
 
 
 def test_splits_override_and_clamp():
@@ -99,6 +107,7 @@ def test_workspace_size_grows_with_batch(B):
     (dict(window_left=0), [100, 100], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "window_left"),
     (dict(window_right=3), [100, 100], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "window_right"),
     (dict(sm_scale=float("nan")), [100, 100], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "sm_scale"),
+    (dict(waves_override=9), [100, 100], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "waves_override"),
 ])
 def test_invalid_parameters_are_named(kw, lens, code, needle):
     with pytest.raises(ba.BlockAttnError) as e:
