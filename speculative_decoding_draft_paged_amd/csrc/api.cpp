@@ -130,28 +130,18 @@ int tiles_for(const blockattn_params* p, int n) {
 }
 
 KernelShape choose_shape(int D, int NB, int R, int waves_override) {
+    // Each wave owns up to two 16-row blocks of the R query rows; WR row-waves stream
+    // the same tiles (the repeat K/V reads hit L2), WT token groups stream different
+    // tiles. D = 64 allows 8 waves per workgroup; D = 128 keeps 4 so a wave may use the
+    // whole register file (one wave per SIMD).
     KernelShape s{};
     s.head_dim = D;
-    if (D == 64 && NB <= 2) {
-        // one wave owns every row and streams its own tiles
-        s.stream = true;
-        s.nbw = NB;
-        s.row_waves = 1;
-        s.token_groups = 4;
-        s.cpw = 0;
-    } else {
-        // row-waves share each tile through LDS: two row blocks per wave for D = 64,
-        // one for D = 128, and at least two waves per tile so a wave stages at most
-        // half of a 16 KiB tile in registers
-        s.stream = false;
-        s.nbw = D == 64 ? 2 : 1;
-        s.row_waves = std::max(D == 64 ? 1 : 2, (NB + s.nbw - 1) / s.nbw);
-        s.token_groups = std::max(1, std::min(4, kMaxWaves / s.row_waves));
-        const int nch = D / 8;
-        const int need = (nch + s.row_waves - 1) / s.row_waves;
-        s.cpw = need <= 4 ? 4 : 8;
-    }
-    if (waves_override > 0) s.token_groups = std::max(1, std::min(waves_override, kMaxWaves / s.row_waves));
+    s.nbw = std::min(NB, 2);
+    s.row_waves = (NB + s.nbw - 1) / s.nbw;
+    s.all_on = NB % s.nbw == 0;
+    const int max_waves = D == 64 ? kMaxWaves : 4;
+    s.token_groups = std::max(1, std::min(4, max_waves / s.row_waves));
+    if (waves_override > 0) s.token_groups = std::max(1, std::min(waves_override, max_waves / s.row_waves));
     s.lds_bytes = attention_lds_bytes(s, R);
     while (s.lds_bytes > kLdsPerCU && s.token_groups > 1) {
         --s.token_groups;
@@ -178,15 +168,15 @@ int build_plan(const blockattn_params* p, const int32_t* lens, blockattn_plan_s*
         nt[b] = tiles_for(p, lens[b]);
         total += (long)nt[b] * H;
     }
+    // Workgroups resident per CU: two waves per SIMD for D = 64, one for D = 128.
     const int waves = pl->shape.row_waves * pl->shape.token_groups;
+    const int waves_per_cu = p->head_dim == 64 ? kMaxWavesPerCU : kMaxWavesPerCU / 2;
     int wg_per_cu = (int)std::max<size_t>(1, kLdsPerCU / std::max<size_t>(pl->shape.lds_bytes, 1));
-    wg_per_cu = std::max(1, std::min(wg_per_cu, kMaxWavesPerCU / waves));
+    wg_per_cu = std::max(1, std::min(wg_per_cu, waves_per_cu / waves));
     const long target_units = (long)kNumCUs * wg_per_cu;
-    // A split's partial state is R*(D+2) floats; 4*D bytes per key are streamed. Keep at
-    // least R/4 tiles per split (partial traffic <= ~1/8 of the KV bytes) and one tile per
-    // token group.
-    const long min_tiles = std::max<long>(pl->shape.token_groups, (pl->R + 3) / 4);
-    const long per_unit = std::max(min_tiles, (total + target_units - 1) / target_units);
+    // Tiles per unit: enough units to fill the GPU, and at least two tiles per token group.
+    const long wt = pl->shape.token_groups;
+    const long per_unit = std::max(2 * wt, (total + target_units - 1) / target_units);
 
     pl->work.clear();
     pl->pair_table.assign((size_t)B * H * 2, 0);

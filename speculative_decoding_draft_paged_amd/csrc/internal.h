@@ -35,7 +35,7 @@ struct KernelArgs {
     int32_t K, Hq, Hkv, g, R, P, stride, num_pages;
     int32_t window_left;   // -1: none
     int32_t window_right;  // -1: every later block key
-    int32_t row_waves;     // WR: waves sharing a tile, each owning NBW row blocks (shared loop only)
+    int32_t row_waves;     // WR: waves streaming the same tiles, each owning NBW row blocks
     int32_t token_groups;  // WT: tile streams per workgroup
     int32_t uniform_splits;  // > 0: every (b, h_kv) has this many splits, unit = pair * S + s (no work list read)
     int32_t merge;         // 1: fold in the block keys after each query (windowed form)
@@ -45,10 +45,9 @@ struct KernelArgs {
 // Chosen kernel shape for a plan.
 struct KernelShape {
     int head_dim;      // 64 or 128
-    bool stream;       // true: per-wave streaming loop (one wave owns all rows); false: LDS-shared tiles
     int nbw;           // 16-row blocks per wave (1 or 2)
-    int cpw;           // shared loop: 1-KiB load chunks per wave per tile (4 or 8)
-    int row_waves;     // WR
+    bool all_on;       // every wave's row blocks hold live rows (R is a multiple of 16 * nbw)
+    int row_waves;     // WR: waves streaming the same tiles, each owning nbw row blocks
     int token_groups;  // WT
     size_t lds_bytes;  // dynamic LDS per workgroup
 };

@@ -12,14 +12,12 @@
 //   - O^T += V^T P^T on the same MFMA with P rounded to bf16; the P operand is
 //     exactly the lane's own S^T accumulator registers (no shuffles). V^T comes
 //     from a row-major V tile in LDS through the transposing LDS read.
-// Two main loops share that tile step:
-//   stream_kernel (R <= 32 rows, one wave owns every row): each wave streams its
-//     own tiles with no workgroup barrier. K goes straight from HBM into the
-//     MFMA A fragments; V goes row-major into a private LDS tile. Two tiles are
-//     in flight per wave, and the page ids of the wave's next 64 half-tiles sit
-//     in one VGPR, read with readlane, so no scalar load sits on the path.
-//   shared_kernel (large R): WR row-waves share each tile through a double-
-//     buffered LDS copy and own some 16-row blocks each.
+// The main loop (stream_kernel) has no workgroup barrier. Each wave owns up to
+// two 16-row blocks of the rows; WR row-waves stream the same tiles (their repeat
+// K/V reads hit L2) and WT token groups stream interleaved tiles of the unit. K
+// goes straight from HBM into the MFMA A fragments; V goes row-major into a
+// private LDS tile. Two tiles are in flight per wave, and the page ids of up to
+// 2048 tiles are staged in LDS once per window, so no scalar load sits on the path.
 // Epilogue: the token groups of the workgroup merge through LDS. A unit that is
 // its request's only split writes the final bf16 output and base-2 LSE itself,
 // and for the windowed form folds in the block keys after each query by the LSE
@@ -151,12 +149,13 @@ struct WaveRows {
     __device__ __forceinline__ void scores(const bf16x8_t (&kf)[2][KK], f32x4_t (&s)[NBW][2]) const {
 #pragma unroll
         for (int n = 0; n < NBW; ++n) {
+            s[n][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            s[n][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (ALL_ON || on[n]) {
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                s[n][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                if (ALL_ON || on[n]) {
+                for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
-                    for (int kk = 0; kk < KK; ++kk)
+                    for (int mb = 0; mb < 2; ++mb)
                         s[n][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mb][kk], qf[n][kk], s[n][mb], 0, 0, 0);
                 }
             }
@@ -164,8 +163,14 @@ struct WaveRows {
     }
 
     // Online softmax update and O^T += V^T P^T for one tile starting at token t0.
+    // m[n] is the reference maximum (log2 units) the row sums are kept relative to.
+    // It only moves when a score exceeds it by more than kRescaleSlack, so the
+    // accumulator rescale is rare and probabilities stay below 2^kRescaleSlack
+    // (exact in fp32 and representable in bf16). The softmax scale is folded into
+    // the exponent's FMA.
     __device__ __forceinline__ void update(const f32x4_t (&s)[NBW][2], const bf16x8_t (&vf)[DB], int t0, float scale,
                                            int quad) {
+        constexpr float kRescaleSlack = 8.f;
         const bool edge = (t0 < lo_max) || (t0 + T - 1 > hi_min);
 #pragma unroll
         for (int n = 0; n < NBW; ++n) {
@@ -174,7 +179,7 @@ struct WaveRows {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) x[mb * 4 + j] = s[n][mb][j] * scale;
+                for (int j = 0; j < 4; ++j) x[mb * 4 + j] = s[n][mb][j];
             if (edge) {
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
@@ -184,29 +189,30 @@ struct WaveRows {
                         if (tok < row_lo[n] || tok > row_hi[n]) x[mb * 4 + j] = kNegInf;
                     }
             }
-            float mx = x[0];
-#pragma unroll
-            for (int k = 1; k < 8; ++k) mx = fmaxf(mx, x[k]);
+            float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m[n], mx);
-            const float m_use = m_new == kNegInf ? 0.f : m_new;
-            const float alpha = fast_exp2(m[n] - m_use);
+            const float mxs = mx * scale;  // scale > 0, so the maximum commutes with it
+            if (mxs > m[n] + kRescaleSlack) {
+                const float alpha = fast_exp2(m[n] - mxs);
+                l[n] *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) acc[n][db] *= alpha;
+                m[n] = mxs;
+            }
+            const float neg_m = m[n] == kNegInf ? 0.f : -m[n];
             bf16x8_t pb;
             float psum = 0.f;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const float p = fast_exp2(x[k] - m_use);
+                const float p = fast_exp2(fmaf(x[k], scale, neg_m));
                 psum += p;
                 pb[k] = (__bf16)p;
             }
-            l[n] = l[n] * alpha + psum;
-            m[n] = m_new;
+            l[n] += psum;
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                acc[n][db] *= alpha;
+            for (int db = 0; db < DB; ++db)
                 acc[n][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pb, acc[n][db], 0, 0, 0);
-            }
         }
     }
 };
@@ -219,8 +225,8 @@ __host__ __device__ constexpr size_t epilogue_floats(int D, int slots_per_group,
 // Merge the wave states of a workgroup, then write a partial, or (only split /
 // last arriver) the final bf16 output and LSE, with the windowed merge.
 template <int D, int NBW, bool WINDOWED, bool ALL_ON>
-__device__ void finish_unit(const KernelArgs& a, const Unit& u, WaveRows<D, NBW, WINDOWED, ALL_ON>& w, int tg, int wr,
-                            int WT, int WR, float* lds) {
+__device__ void finish_unit(const KernelArgs& a, const Unit& u, WaveRows<D, NBW, WINDOWED, ALL_ON>& w, int tg,
+                            int wr, int WT, int WR, float* lds) {
     constexpr int DB = D / 16, MP = D + 4;
     const int tid = threadIdx.x, nthreads = blockDim.x;
     const int lane = tid & 63, r16 = lane & 15, quad = lane >> 4;
@@ -352,8 +358,8 @@ __device__ void finish_unit(const KernelArgs& a, const Unit& u, WaveRows<D, NBW,
 // global load of the loop sits at a fixed, unconditional place (tile indices past
 // the wave's last tile are clamped to it), which keeps the compiler's wait counts
 // exact: the wait for one tile never drains the tile behind it.
-template <int D, int NBW, bool WINDOWED>
-__global__ __launch_bounds__(512) void stream_kernel(const KernelArgs a) {
+template <int D, int NBW, bool WINDOWED, bool ALL_ON, int MAXT>
+__global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
     constexpr int KK = D / 32, DB = D / 16;
     constexpr int VCH = D / 16;   // 1-KiB chunks of the V tile (16 bytes per lane each)
     constexpr int VP = D + 8;     // padded row pitch of the V tile in LDS (bf16 elements)
@@ -364,12 +370,14 @@ __global__ __launch_bounds__(512) void stream_kernel(const KernelArgs a) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
     const int r16 = lane & 15, quad = lane >> 4;
-    const int WT = a.token_groups;
+    const int WT = a.token_groups, WR = a.row_waves;
+    const int tg = wave / WR, wr = wave - (wave / WR) * WR;  // token group, row group
     const Unit u = decode_unit<WINDOWED>(a);
-    WaveRows<D, NBW, WINDOWED, true> w;
-    w.init(a, u, 0, lane);
+    WaveRows<D, NBW, WINDOWED, ALL_ON> w;
+    w.init(a, u, wr * NBW, lane);
+    // LDS: [one V tile per wave] [page-id window]
     uint16_t* vlds = lds + (size_t)wave * T * VP;
-    int* pid_tab = reinterpret_cast<int*>(lds + (size_t)WT * T * VP);
+    int* pid_tab = reinterpret_cast<int*>(lds + (size_t)WT * WR * T * VP);
 
     const int32_t* pt_row = a.page_table + (size_t)u.b * a.stride;
     const int last_page = (u.N - 1) / a.P;
@@ -402,14 +410,14 @@ __global__ __launch_bounds__(512) void stream_kernel(const KernelArgs a) {
             }
         }
         __syncthreads();
-        const int nk = span > wave ? (span - wave + WT - 1) / WT : 0;
+        const int nk = span > tg ? (span - tg + WT - 1) / WT : 0;
         if (nk == 0) continue;
 
         auto issue = [&](TileRegs& t, int k) {
             const int kc = min(k, nk - 1);
-            const int j = 2 * (wave + kc * WT);
+            const int j = 2 * (tg + kc * WT);
             const int pid0 = pid_tab[j], pid1 = pid_tab[j + 1];
-            const int t0 = (win + wave + kc * WT) * T;
+            const int t0 = (win + tg + kc * WT) * T;
             const size_t base0 = ((size_t)pid0 * a.Hkv + u.hk) * head_elems + (size_t)(t0 % a.P) * D;
             const size_t base1 = ((size_t)pid1 * a.Hkv + u.hk) * head_elems + (size_t)((t0 + 16) % a.P) * D;
 #pragma unroll
@@ -427,14 +435,23 @@ __global__ __launch_bounds__(512) void stream_kernel(const KernelArgs a) {
         };
 
         auto consume = [&](TileRegs& t, int k, bool valid, bool reissue) {
-            const int t0 = (win + wave + k * WT) * T;
+            const int t0 = (win + tg + k * WT) * T;
             f32x4_t s[NBW][2];
             if (valid) {
+                if (t0 + T > u.N) {  // the tail tile: rows past the sequence end become zeros
 #pragma unroll
-                for (int c = 0; c < VCH; ++c) {
-                    const int row = c * RPC + (lane * 8) / D;
-                    const int col = (lane * 8) % D;
-                    *(u32x4_t*)(vlds + row * VP + col) = (t0 + row < u.N) ? t.v[c] : u32x4_t{0u, 0u, 0u, 0u};
+                    for (int c = 0; c < VCH; ++c) {
+                        const int row = c * RPC + (lane * 8) / D;
+                        const int col = (lane * 8) % D;
+                        *(u32x4_t*)(vlds + row * VP + col) = (t0 + row < u.N) ? t.v[c] : u32x4_t{0u, 0u, 0u, 0u};
+                    }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < VCH; ++c) {
+                        const int row = c * RPC + (lane * 8) / D;
+                        const int col = (lane * 8) % D;
+                        *(u32x4_t*)(vlds + row * VP + col) = t.v[c];
+                    }
                 }
                 bf16x8_t kf[2][KK];
 #pragma unroll
@@ -472,104 +489,6 @@ __global__ __launch_bounds__(512) void stream_kernel(const KernelArgs a) {
             consume(ta, k, true, true);
             consume(tb, k + 1, k + 1 < nk, false);
         }
-    }
-    finish_unit(a, u, w, wave, 0, WT, 1, reinterpret_cast<float*>(lds));
-}
-
-// ---------------------------------------------------------------------------------
-// LDS-shared main loop: WR row-waves share each tile (for R > 32), WT token groups.
-template <int D, int NBW, int CPW, bool WINDOWED>
-__global__ __launch_bounds__(512) void shared_kernel(const KernelArgs a) {
-    constexpr int KP = D + 8;  // padded pitch of the K tile
-    constexpr int VP = D + 8;  // padded pitch of the row-major V tile
-    constexpr int KT = T * KP;
-    constexpr int BUF = KT + T * VP;
-    constexpr int NCH = D / 8;  // 1-KiB chunks of a tile, K then V
-    constexpr int HALF = NCH / 2;
-    constexpr int KK = D / 32, DB = D / 16;
-
-    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar) index
-    const int WR = a.row_waves, WT = a.token_groups;
-    const int tg = wave / WR, wr = wave - (wave / WR) * WR;
-    const int r16 = lane & 15, quad = lane >> 4;
-    uint16_t* tg_lds = lds + (size_t)tg * 2 * BUF;
-    const Unit u = decode_unit<WINDOWED>(a);
-    WaveRows<D, NBW, WINDOWED> w;
-    w.init(a, u, wr * NBW, lane);
-
-    const int32_t* pt_row = a.page_table + (size_t)u.b * a.stride;
-    const int last_page = (u.N - 1) / a.P;
-    const size_t head_elems = (size_t)a.P * D;
-    u32x4_t pre[CPW];
-
-    auto prefetch = [&](int tile) {
-        const int t0 = tile * T;
-        const int pid0 = clampi(pt_row[min(t0 / a.P, last_page)], 0, a.num_pages - 1);
-        const int pid1 = clampi(pt_row[min((t0 + 16) / a.P, last_page)], 0, a.num_pages - 1);
-        const size_t base0 = ((size_t)pid0 * a.Hkv + u.hk) * head_elems + (size_t)(t0 % a.P) * D;
-        const size_t base1 = ((size_t)pid1 * a.Hkv + u.hk) * head_elems + (size_t)((t0 + 16) % a.P) * D;
-#pragma unroll
-        for (int ci = 0; ci < CPW; ++ci) {
-            const int c = wr + ci * WR;
-            if (c < NCH) {
-                const bool is_v = c >= HALF;
-                const int cc = is_v ? c - HALF : c;
-                const int off = cc * 512 + lane * 8;
-                const int row = off / D, col = off - (off / D) * D;
-                const bool h1 = row >= 16;
-                pre[ci] = ldg16((is_v ? a.vc : a.kc) + (h1 ? base1 : base0) + (size_t)(row - (h1 ? 16 : 0)) * D + col);
-            }
-        }
-    };
-    auto store = [&](int tile, uint16_t* buf) {
-        const int t0 = tile * T;
-#pragma unroll
-        for (int ci = 0; ci < CPW; ++ci) {
-            const int c = wr + ci * WR;
-            if (c < NCH) {
-                const bool is_v = c >= HALF;
-                const int cc = is_v ? c - HALF : c;
-                const int off = cc * 512 + lane * 8;
-                const int row = off / D, col = off - (off / D) * D;
-                if (!is_v) *(u32x4_t*)(buf + row * KP + col) = pre[ci];
-                else *(u32x4_t*)(buf + KT + row * VP + col) = (t0 + row < u.N) ? pre[ci] : u32x4_t{0u, 0u, 0u, 0u};
-            }
-        }
-    };
-    auto compute = [&](int tile, const uint16_t* buf) {
-        bf16x8_t kf[2][KK];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-                kf[mb][kk] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(buf + (mb * 16 + r16) * KP + kk * 32 + quad * 8));
-        f32x4_t s[NBW][2];
-        w.scores(kf, s);
-        bf16x8_t vf[DB];
-        const uint16_t* vrow = buf + KT + (size_t)(4 * quad + (r16 >> 2)) * VP + 4 * (r16 & 3);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const u32x2_t lo = lds_read_tr16(vrow + db * 16);
-            const u32x2_t hi = lds_read_tr16(vrow + 16 * VP + db * 16);
-            vf[db] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
-        }
-        w.update(s, vf, tile * T, a.scale_log2, quad);
-    };
-
-    const int n_iter = u.uhi > u.ulo ? (u.uhi - u.ulo + WT - 1) / WT : 0;
-    int tile = u.ulo + tg;
-    if (n_iter > 0 && tile < u.uhi) prefetch(tile);
-    for (int it = 0; it < n_iter; ++it) {
-        uint16_t* buf = tg_lds + (it & 1) * BUF;
-        const bool valid = tile < u.uhi;
-        if (valid) store(tile, buf);
-        __syncthreads();
-        const int next = tile + WT;
-        if (next < u.uhi) prefetch(next);
-        if (valid) compute(tile, buf);
-        tile = next;
     }
     finish_unit(a, u, w, tg, wr, WT, WR, reinterpret_cast<float*>(lds));
 }
@@ -686,31 +605,24 @@ hipError_t launch_with_lds(F fn, int units, int threads, size_t lds, const Kerne
     return hipGetLastError();
 }
 
-template <int D, int NBW, bool W>
+template <int D, int NBW, bool W, bool ALL_ON>
 hipError_t launch_stream(const KernelShape& s, int units, const KernelArgs& args, hipStream_t stream) {
     static size_t granted = 0;
-    return launch_with_lds(stream_kernel<D, NBW, W>, units, 64 * s.token_groups, s.lds_bytes, args, stream, &granted);
-}
-
-template <int D, int NBW, int CPW, bool W>
-hipError_t launch_shared(const KernelShape& s, int units, const KernelArgs& args, hipStream_t stream) {
-    static size_t granted = 0;
-    return launch_with_lds(shared_kernel<D, NBW, CPW, W>, units, 64 * s.row_waves * s.token_groups, s.lds_bytes,
-                           args, stream, &granted);
+    constexpr int MAXT = D == 64 ? 512 : 256;  // D = 128 keeps workgroups small so a wave may use 512 registers
+    return launch_with_lds(stream_kernel<D, NBW, W, ALL_ON, MAXT>, units, 64 * s.row_waves * s.token_groups,
+                           s.lds_bytes, args, stream, &granted);
 }
 
 template <bool W>
 hipError_t dispatch(const KernelShape& s, int units, const KernelArgs& args, hipStream_t stream) {
-    if (s.stream) {
-        if (s.head_dim == 64 && s.nbw == 1) return launch_stream<64, 1, W>(s, units, args, stream);
-        if (s.head_dim == 64 && s.nbw == 2) return launch_stream<64, 2, W>(s, units, args, stream);
-        return hipErrorInvalidValue;
-    }
-#define BA_CASE(D_, NBW_, CPW_) \
-    if (s.head_dim == D_ && s.nbw == NBW_ && s.cpw == CPW_) return launch_shared<D_, NBW_, CPW_, W>(s, units, args, stream);
-    BA_CASE(64, 2, 4)
-    BA_CASE(128, 1, 4)
-    BA_CASE(128, 1, 8)
+#define BA_CASE(D_, NBW_)                                                                               \
+    if (s.head_dim == D_ && s.nbw == NBW_)                                                              \
+        return s.all_on ? launch_stream<D_, NBW_, W, true>(s, units, args, stream)                      \
+                        : launch_stream<D_, NBW_, W, false>(s, units, args, stream);
+    BA_CASE(64, 1)
+    BA_CASE(64, 2)
+    BA_CASE(128, 1)
+    BA_CASE(128, 2)
 #undef BA_CASE
     return hipErrorInvalidValue;
 }
@@ -720,11 +632,8 @@ hipError_t dispatch(const KernelShape& s, int units, const KernelArgs& args, hip
 size_t attention_lds_bytes(const KernelShape& s, int R) {
     (void)R;
     const int D = s.head_dim;
-    size_t loop;
-    if (s.stream)
-        loop = (size_t)s.token_groups * kTileTokens * (D + 8) * sizeof(uint16_t) + 2 * kPidWindow * sizeof(int);
-    else
-        loop = (size_t)s.token_groups * 2 * ((size_t)kTileTokens * (D + 8) * 2) * sizeof(uint16_t);
+    const size_t loop = ((size_t)s.token_groups * s.row_waves * kTileTokens) * (D + 8) * sizeof(uint16_t) +
+                        2 * kPidWindow * sizeof(int);
     const size_t epi = epilogue_floats(D, s.row_waves * s.nbw, s.token_groups) * sizeof(float);
     return loop > epi ? loop : epi;
 }

@@ -74,8 +74,8 @@ def run(dc: DeviceCase, *, window_left=None, window_right=None, splits=0, plan_l
     fwd = ba.blockattn_forward if prm.window_left == -1 else ba.blockattn_windowed_forward
     fwd(plan, dc.q, dc.k, dc.v, dc.page_table, dc.seq_lens, ws, out, lse)
     torch.cuda.synchronize()
-    # A second call on the same plan and workspace must give the same bits: the split
-    # counters of the fused combine reset themselves.
+    # A second call on the same plan and workspace must give the same bits: nothing a
+    # call leaves in the workspace may leak into the next one.
     first = out.clone()
     first_lse = lse.clone() if lse is not None else None
     fwd(plan, dc.q, dc.k, dc.v, dc.page_table, dc.seq_lens, ws, out, lse)

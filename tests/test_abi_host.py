@@ -57,7 +57,7 @@ def test_split_heuristic_fills_the_gpu_and_bounds_partials():
     assert small["units"] >= 256
     big = plan_info(params(batch=32, num_q_heads=64, num_kv_heads=16), [131079] * 32)
     assert big["max_splits"] == 1 and big["units"] == 512
-    # every split keeps >= R/4 tiles of keys
+    # every token group gets at least two tiles
     tiny = plan_info(params(batch=1), [200])
     assert tiny["max_splits"] == 1
 
@@ -67,7 +67,7 @@ def test_waves_override():
     assert plan_info(params(waves_override=1), [5000, 5000])["waves_per_unit"] == 1
     w = dict(head_dim=128, page_size=64, num_q_heads=16, num_kv_heads=1, window_left=4096, block_size=7)
     info = plan_info(params(**w, waves_override=8), [8199, 8199])
-    assert info["row_waves"] == 7 and info["token_groups"] == 1
+    assert info["row_waves"] == 4 and info["token_groups"] == 1
 
 
 def test_splits_override_and_clamp():
@@ -83,7 +83,7 @@ def test_windowed_plan_merge_flag():
     assert plan_info(params(**w, block_size=1, window_right=-1), [8193, 8193])["merge_active"] == 0
     assert plan_info(params(**w, block_size=7, window_right=0), [8199, 8199])["merge_active"] == 0
     info = plan_info(params(**w, block_size=7, window_right=-1), [8199, 8199])
-    assert info["kind"] == 1 and info["row_waves"] == 7
+    assert info["kind"] == 1 and info["row_waves"] == 4
 
 
 @pytest.mark.parametrize("B", [1, 2, 32, 33, 200])
