@@ -5,14 +5,16 @@ Workload (default): the Kimi-style TP8 rank of a 64q/16kv GQA drafter, i.e.
 8 q / 2 kv heads, head_dim 64, block K = 7, 128K-token contexts, page 32, HND
 bf16 pools, B = 8 requests with disjoint shuffled page ranges; synthetic N(0,1)
 data from the seeded generator. One step = one blockattn_forward call for the
-whole batch (plan once, outside timing): the split-KV partial kernel and the
-LSE combine.
+whole batch (plan once, outside timing): the paged attention kernel and, when
+the plan splits a request's keys, the LSE combine.
 
 Timing: the K timed steps are one captured HIP graph, replayed between two
 device synchronisations; each step reads the next of M copies of the K/V pools
 (M * pool >= 1 GiB) so the 256 MB Infinity Cache cannot serve repeats. HIP
-events recorded around every partial-kernel launch give that kernel's average
-duration (a separate pass of K eager calls), from which the roofline fraction is computed.
+events recorded around every attention-kernel launch give that kernel's average
+duration (a separate pass of K eager calls), from which the roofline fraction is
+computed. HBM traffic per launch comes from a committed rocprofv3 counter summary
+of the same kernel source (null when the source has changed since).
 
 Output: one JSON line (metric, value in GB/s of algorithmic KV bytes, ...,
 roofline, cpu_baseline). The cpu_baseline leg times the fp64 oracle on a
@@ -193,7 +195,7 @@ def run_case(case, steps, warmup, threads, graph=True, splits=0, waves=0):
         raise RuntimeError("timed run output differs from the warm-up output")
     total_ms = hip.elapsed_ms(ga, gb)
 
-    # Kernel timing: HIP events recorded by the library right around every partial-kernel
+    # Kernel timing: HIP events recorded by the library right around every attention-kernel
     # launch, on the stream it launches on, over `steps` eager calls.
     before, after = hip.create(steps), hip.create(steps)
     for i in range(steps):
@@ -224,27 +226,74 @@ def run_case(case, steps, warmup, threads, graph=True, splits=0, waves=0):
     return res, inp, out
 
 
-def stream_reference():
-    """Achievable read bandwidth: torch reductions over 2 GiB (8 rotating 256 MiB slices)."""
+COPY_ELEMS = 1 << 28  # float32 elements of the reference copy: 1 GiB read + 1 GiB written per launch
+
+
+def copy_reference(reps=10):
+    """A plain elementwise kernel of known traffic: y = -x over 1 GiB of float32.
+
+    Its HBM rate (read + written bytes / time) is the box's achievable streaming
+    reference, and its PMC byte counters calibrate FETCH_SIZE / WRITE_SIZE (the
+    kernel moves exactly 1 GiB each way per launch)."""
     import torch
 
-    x = torch.ones(1 << 30, dtype=torch.bfloat16, device="cuda")
-    res = {}
-    for name, fn in (("sum_bf16", lambda t: t.sum(dtype=torch.float32)),
-                     ("amax_bf16", lambda t: t.amax())):
-        for _ in range(3):
-            fn(x)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(10):
-            fn(x)
-        torch.cuda.synchronize()
-        dt = (time.perf_counter() - t0) / 10
-        res[name] = round(x.numel() * 2 / dt / 1e9, 1)
-    del x
+    x = torch.ones(COPY_ELEMS, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(2):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    res = {"kernel": "torch.neg float32, 1 GiB in + 1 GiB out", "us": round(dt * 1e6, 1),
+           "gbs_read_plus_write": round(2 * x.numel() * 4 / dt / 1e9, 1)}
+    del x, y
     torch.cuda.empty_cache()
-    log(f"[bench] streaming-read reference (GB/s): {res}")
+    log(f"[bench] copy reference: {res}")
     return res
+
+
+def _counter_rows(path):
+    """Rows (kernel name, counter, value) of a rocprofv3 counter_collection.csv (file or folder)."""
+    import csv
+    import glob
+
+    files = [path] if os.path.isfile(path) else sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"),
+                                                                 recursive=True))
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {path}")
+    rows = []
+    for fn in files:
+        with open(fn, newline="") as f:
+            for r in csv.DictReader(f):
+                rows.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def pmc_summary(case_name, fetch_path, write_path):
+    """Turn a FETCH_SIZE run and a WRITE_SIZE run into HBM bytes per attention-kernel launch.
+
+    Both counters are KiB per dispatch. Each is scaled by the factor that maps the
+    reference copy's reading onto its known 1 GiB, then averaged over the
+    stream_kernel dispatches of the run."""
+    out = {"case": case_name, "kernel_digest": kernel_source_digest()}
+    for tag, path, counter in (("fetch", fetch_path, "FETCH_SIZE"), ("write", write_path, "WRITE_SIZE")):
+        rows = [r for r in _counter_rows(path) if r[1] == counter]
+        att = [v for k, _, v in rows if "stream_kernel" in k]
+        ref = [v for k, _, v in rows if "neg" in k.lower()]
+        if not att or not ref:
+            raise SystemExit(f"{path}: {counter} rows for stream_kernel ({len(att)}) or the copy ({len(ref)}) missing")
+        ref_kib = sum(ref) / len(ref)
+        factor = (COPY_ELEMS * 4 / 1024) / ref_kib
+        out[f"{tag}_kib_raw"] = round(sum(att) / len(att), 1)
+        out[f"{tag}_copy_kib_raw"] = round(ref_kib, 1)
+        out[f"{tag}_scale"] = round(factor, 5)
+        out[f"{tag}_bytes_per_launch"] = int(sum(att) / len(att) * 1024 * factor)
+        out[f"{tag}_dispatches"] = len(att)
+    out["hbm_bytes_per_launch"] = out["fetch_bytes_per_launch"] + out["write_bytes_per_launch"]
+    return out
 
 
 def cpu_baseline(case, inp, gpu_out, kv_total, budget_s):
@@ -299,11 +348,20 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--splits", type=int, default=0, help="force the split count per (request, kv head)")
     ap.add_argument("--waves", type=int, default=0, help="force the tile-streaming waves per workgroup")
-    ap.add_argument("--stream-reference", action="store_true",
-                    help="also time plain streaming reads of 2 GiB (achievable HBM read bandwidth)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="run a plain 1 GiB device copy 5 times (reference kernel for PMC byte counters)")
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="also time a plain 1 GiB elementwise copy (achievable HBM rate; PMC calibration kernel)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH", "WRITE"),
+                    help="no GPU: read two rocprofv3 --pmc outputs (FETCH_SIZE, WRITE_SIZE) of a --copy-reference "
+                         "run of --case and write profiles/pmc_partial_<case>.json")
     args = ap.parse_args()
+
+    if args.pmc_summary:
+        rec = pmc_summary(args.case, *args.pmc_summary)
+        with open(os.path.join(ROOT, "profiles", f"pmc_partial_{args.case}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(json.dumps(rec))
+        return
 
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU; the path shards by request or kv head "
@@ -315,13 +373,6 @@ def main():
     from synth.configs import cases_for_config, find_case
 
     threads = min(16, len(os.sched_getaffinity(0)))
-    if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log("[bench] copy calibration: 5 x 1 GiB device copies done")
 
     case = find_case(args.case)
     res, inp, out = run_case(case, args.steps, args.warmup, threads, graph=not args.eager, splits=args.splits,
@@ -329,7 +380,7 @@ def main():
     kvb = res["kv_bytes"]
     value = kvb / (res["step_ms"] * 1e-3) / 1e9
     achieved = kvb / (res["partial_ms"] * 1e-3) / 1e9
-    log(f"[bench] {case.name}: step {res['step_ms'] * 1e3:.1f} us, partial kernel {res['partial_ms'] * 1e3:.1f} us "
+    log(f"[bench] {case.name}: step {res['step_ms'] * 1e3:.1f} us, attention kernel {res['partial_ms'] * 1e3:.1f} us "
         f"(min {res['partial_ms_min'] * 1e3:.1f}), {value:.0f} GB/s per step, {achieved:.0f} GB/s in the partial "
         f"kernel, units {res['units']}, splits {res['max_splits']}, graph {res['graph']}")
 
@@ -348,7 +399,7 @@ def main():
                 f"{r['partial_gbs']:7.0f} GB/s  units {r['units']}")
             torch.cuda.empty_cache()
 
-    stream_ref = stream_reference() if args.stream_reference else None
+    copy_ref = copy_reference() if args.copy_reference else None
     traffic = load_traffic(case.name, kvb)
     line = {
         "metric": METRIC,
@@ -375,12 +426,12 @@ def main():
                    "max_splits": res["max_splits"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "partial_kernel (split-KV partial attention)",
+                     "kernel": "stream_kernel (split-KV paged attention)",
                      "kernel_us": round(res["partial_ms"] * 1e3, 2), "kernel_events": res["kernel_timing"]},
         "cpu_baseline": None,
     }
-    if stream_ref is not None:
-        line["stream_reference"] = stream_ref
+    if copy_ref is not None:
+        line["copy_reference"] = copy_ref
     if sweep is not None:
         line["sweep"] = [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()} for r in sweep]
     if not args.no_cpu_baseline:
