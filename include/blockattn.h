@@ -10,12 +10,13 @@
  *    request sees the same N_b = seq_lens[b] keys (TensorRT-LLM PR #20374,
  *    "non-causal unwindowed DFlash block attention", Description: with no mask
  *    all block queries attend the same seq_lens_after keys).
- *  - blockattn_windowed_forward: the non-causal windowed form, served as a
- *    causal windowed decode that yields a base-2 LSE, followed by a
- *    log-sum-exp merge of the block keys that follow each query (TensorRT-LLM
- *    PR #21130, DSpark non-causal windowed draft layer, Description items 1-2).
- *    With K = 1 or window_right = 0 no block key follows any query, the merge
- *    is skipped and the causal result is returned as is.
+ *  - blockattn_windowed_forward: the non-causal windowed form: a causal
+ *    windowed decode with a base-2 LSE, and the log-sum-exp merge of the block
+ *    keys that follow each query (TensorRT-LLM PR #21130, DSpark non-causal
+ *    windowed draft layer, Description items 1-2). Those keys lie in the tiles
+ *    the decode already streams, so the merge is done by the decode's own online
+ *    softmax update rather than by a second pass. With K = 1 or window_right = 0
+ *    no block key follows any query and the causal result is returned as is.
  *
  * Definitions (p = N_b - K + i is the absolute position of block query i):
  *   s_j  = sm_scale * <q[b,i,h,:], k_j>, with k_j read through the page table
@@ -90,13 +91,16 @@ typedef struct blockattn_plan_info {
     int32_t kind;              /* 0 unwindowed, 1 windowed */
     int32_t units;             /* work units (workgroups) of the split-KV partial kernel */
     int32_t max_splits;        /* largest split count of any (request, kv head) */
-    int32_t merge_active;      /* 1 when the windowed future-block-key merge runs */
+    int32_t merge_active;      /* 1 when block keys after a query join its key set (windowed, K > 1,
+                                  window_right != 0) */
     int32_t waves_per_unit;    /* wavefronts per workgroup of the partial kernel */
     int32_t token_groups;      /* wavefronts streaming different tiles inside one workgroup */
     int32_t row_waves;         /* wavefronts sharing one tile, each owning some query rows */
     int32_t uploaded;          /* 1 once the work list has been copied into a workspace */
     int32_t combine_launch;    /* 1: a combine kernel follows the attention kernel (some request has
                                   more than one split); 0: every split wrote its output directly */
+    int32_t shared_tiles;      /* 1: each workgroup loads a tile once into LDS for all its row waves
+                                  (R > 32); 0: each wave streams its own tiles */
     size_t workspace_bytes;    /* bytes the plan needs */
 } blockattn_plan_info_t;
 
@@ -137,15 +141,16 @@ int blockattn_forward(blockattn_plan_t plan, const void* q, const void* k_cache,
 
 /*
  * Non-causal windowed block attention (the plan must have window_left >= 1):
- * a causal windowed split-KV decode, its combine, and the fused merge of the
- * block keys after each query. Same arguments as blockattn_forward; lse is
- * required and receives the final, merged base-2 LSE.
+ * the causal windowed split-KV decode with the block keys after each query
+ * folded into the same online softmax (the log-sum-exp merge, applied to the
+ * running state), then the split combine. Same arguments as blockattn_forward;
+ * lse is required and receives the final, merged base-2 LSE.
  */
 int blockattn_windowed_forward(blockattn_plan_t plan, const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* page_table, const int32_t* seq_lens, void* workspace, void* out,
                                float* lse, void* stream);
 
-/* Describe the plan (path taken, units, splits, merge on or off). */
+/* Describe the plan (path taken, units, splits, future block keys on or off). */
 int blockattn_plan_info(blockattn_plan_t plan, blockattn_plan_info_t* info);
 
 /*

@@ -39,7 +39,6 @@ int fail(int code, const std::string& msg) {
 
 constexpr int kNumCUs = 256;
 constexpr size_t kLdsPerCU = 160 * 1024;
-constexpr int kMaxWavesPerCU = 8;  // two waves per SIMD at ~200 VGPRs
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -122,7 +121,7 @@ int validate(const blockattn_params* p, const int32_t* lens) {
 }
 
 // Key tiles a request needs: 32-token tiles covering the union of its rows' key sets
-// (the causal windows for the windowed form; the future keys are merged later).
+// (for the windowed form the causal windows and the block keys after each query).
 int tiles_for(const blockattn_params* p, int n) {
     const int c = n - p->block_size;
     const int lo = p->window_left > 0 ? std::max(0, c - p->window_left + 1) : 0;
@@ -130,18 +129,36 @@ int tiles_for(const blockattn_params* p, int n) {
 }
 
 KernelShape choose_shape(int D, int NB, int R, int waves_override) {
-    // Each wave owns up to two 16-row blocks of the R query rows; WR row-waves stream
-    // the same tiles (the repeat K/V reads hit L2), WT token groups stream different
-    // tiles. D = 64 allows 8 waves per workgroup; D = 128 keeps 4 so a wave may use the
-    // whole register file (one wave per SIMD).
+    // Each wave owns up to two 16-row blocks of the R query rows. With one row-wave
+    // (R <= 32), WT token groups of the workgroup stream different tiles, each wave
+    // loading its own (stream_kernel). With WR > 1 row-waves the workgroup loads each
+    // tile once into an LDS ring that every row-wave reads (shared_kernel). D = 64
+    // allows 8 waves per workgroup; D = 128 keeps 4 so a wave may use the whole
+    // register file (one wave per SIMD).
     KernelShape s{};
     s.head_dim = D;
     s.nbw = std::min(NB, 2);
     s.row_waves = (NB + s.nbw - 1) / s.nbw;
     s.all_on = NB % s.nbw == 0;
+    s.waves_per_simd = D == 64 ? 2 : 1;
     const int max_waves = D == 64 ? kMaxWaves : 4;
-    s.token_groups = std::max(1, std::min(4, max_waves / s.row_waves));
-    if (waves_override > 0) s.token_groups = std::max(1, std::min(waves_override, max_waves / s.row_waves));
+    // More than one row-wave: the workgroup shares each tile through LDS, one token stream.
+    s.shared = s.row_waves > 1;
+    s.token_groups = s.shared ? 1 : std::max(1, std::min(4, max_waves / s.row_waves));
+    if (s.shared && D == 128) {
+        // One row block per wave and up to 8 waves (two per SIMD, each within 256
+        // registers) from five row blocks on, so two waves per SIMD hide each other's
+        // latency; fewer rows keep two blocks per wave. waves_override picks the
+        // waves per workgroup: rows per wave = ceil(blocks / waves), 1 or 2.
+        int wv = NB >= 5 ? NB : s.row_waves;
+        if (waves_override > 0) wv = std::max((NB + 1) / 2, std::min(waves_override, NB));
+        s.nbw = (NB + wv - 1) / wv;
+        s.row_waves = (NB + s.nbw - 1) / s.nbw;
+        s.all_on = NB % s.nbw == 0;
+        s.waves_per_simd = s.nbw == 1 ? 2 : 1;
+    } else if (waves_override > 0 && !s.shared) {
+        s.token_groups = std::max(1, std::min(waves_override, max_waves / s.row_waves));
+    }
     s.lds_bytes = attention_lds_bytes(s, R);
     while (s.lds_bytes > kLdsPerCU && s.token_groups > 1) {
         --s.token_groups;
@@ -168,15 +185,41 @@ int build_plan(const blockattn_params* p, const int32_t* lens, blockattn_plan_s*
         nt[b] = tiles_for(p, lens[b]);
         total += (long)nt[b] * H;
     }
-    // Workgroups resident per CU: two waves per SIMD for D = 64, one for D = 128.
+    // Workgroups resident per CU, from the kernel's waves per SIMD and its LDS.
     const int waves = pl->shape.row_waves * pl->shape.token_groups;
-    const int waves_per_cu = p->head_dim == 64 ? kMaxWavesPerCU : kMaxWavesPerCU / 2;
+    const int waves_per_cu = 4 * pl->shape.waves_per_simd;
     int wg_per_cu = (int)std::max<size_t>(1, kLdsPerCU / std::max<size_t>(pl->shape.lds_bytes, 1));
     wg_per_cu = std::max(1, std::min(wg_per_cu, waves_per_cu / waves));
-    const long target_units = (long)kNumCUs * wg_per_cu;
-    // Tiles per unit: enough units to fill the GPU, and at least two tiles per token group.
+    const long slots = (long)kNumCUs * wg_per_cu;
+    // Tiles per unit (at least two per token group): the value that minimises an
+    // estimate of the makespan. Units run in rounds of `slots` resident workgroups; a
+    // round costs its largest unit's tiles plus a fixed start-up and epilogue cost,
+    // and splitting any request adds the combine launch. Both costs are in tiles.
+    constexpr long kUnitCost = 8, kCombineCost = 8;
     const long wt = pl->shape.token_groups;
-    const long per_unit = std::max(2 * wt, (total + target_units - 1) / target_units);
+    long max_nt = 1;
+    for (int b = 0; b < B; ++b) max_nt = std::max<long>(max_nt, nt[b]);
+    long per_unit = std::max(2 * wt, (total + slots - 1) / slots);
+    if (p->splits_override <= 0 && per_unit < max_nt) {
+        long best = -1, best_cost = 0;
+        for (long pu = per_unit;; pu = std::min(max_nt, std::max(pu + 1, pu * 9 / 8))) {
+            long units = 0, largest = 0;
+            bool split = false;
+            for (int b = 0; b < B; ++b) {
+                const long S = std::max(1L, std::min<long>((nt[b] + pu - 1) / pu, nt[b]));
+                units += S * H;
+                largest = std::max(largest, (nt[b] + S - 1) / S);
+                split = split || S > 1;
+            }
+            const long cost = (units + slots - 1) / slots * (largest + kUnitCost) + (split ? kCombineCost : 0);
+            if (best < 0 || cost < best_cost) {
+                best = pu;
+                best_cost = cost;
+            }
+            if (pu >= max_nt) break;
+        }
+        per_unit = best;
+    }
 
     pl->work.clear();
     pl->pair_table.assign((size_t)B * H * 2, 0);
@@ -259,7 +302,6 @@ int run_forward(blockattn_plan_t plan, const void* q, const void* k, const void*
     ka.row_waves = plan->shape.row_waves;
     ka.token_groups = plan->shape.token_groups;
     ka.uniform_splits = plan->uniform_splits;
-    ka.merge = plan->merge_active ? 1 : 0;
     ka.scale_log2 = (float)((double)p.sm_scale * 1.4426950408889634);
 
     hipError_t e = hipSuccess;
@@ -362,6 +404,7 @@ int blockattn_plan_info(blockattn_plan_t plan, blockattn_plan_info_t* info) {
     info->row_waves = plan->shape.row_waves;
     info->uploaded = plan->uploaded ? 1 : 0;
     info->combine_launch = plan->max_splits > 1 ? 1 : 0;
+    info->shared_tiles = plan->shape.shared ? 1 : 0;
     info->workspace_bytes = plan->lay.total;
     return BLOCKATTN_OK;
 }

@@ -8,8 +8,7 @@ namespace blockattn {
 
 constexpr int kTileTokens = 32;   // keys per tile: one MFMA K-step of PV, two 16-token M blocks of QK^T
 constexpr int kMaxRowBlocks = 8;  // R = K * group <= 128 query rows per kv head
-constexpr int kMaxWaves = 8;      // wavefronts per workgroup of the attention kernel
-constexpr int kMaxFuture = 16;    // future block keys per row the merge can hold (K <= 16)
+constexpr int kMaxWaves = 8;      // wavefronts per workgroup of the attention kernels
 constexpr int kPidWindow = 2048;     // tiles whose page ids the streaming kernel stages in LDS at a time
 
 // One unit of split-KV work. Tiles [lo, hi) of the key range of (b, h_kv) are derived on
@@ -38,7 +37,6 @@ struct KernelArgs {
     int32_t row_waves;     // WR: waves streaming the same tiles, each owning NBW row blocks
     int32_t token_groups;  // WT: tile streams per workgroup
     int32_t uniform_splits;  // > 0: every (b, h_kv) has this many splits, unit = pair * S + s (no work list read)
-    int32_t merge;         // 1: fold in the block keys after each query (windowed form)
     float scale_log2;      // sm_scale * log2(e)
 };
 
@@ -49,6 +47,8 @@ struct KernelShape {
     bool all_on;       // every wave's row blocks hold live rows (R is a multiple of 16 * nbw)
     int row_waves;     // WR: waves streaming the same tiles, each owning nbw row blocks
     int token_groups;  // WT
+    bool shared;       // row_waves > 1: the workgroup loads each tile once into an LDS ring (shared_kernel)
+    int waves_per_simd;  // occupancy the kernel's register use allows (1 or 2)
     size_t lds_bytes;  // dynamic LDS per workgroup
 };
 

@@ -1,35 +1,39 @@
 // gfx950 kernels for draft-block paged attention.
 //
-// attention kernels (split-KV partial attention and its epilogue). One
-// workgroup = one work unit: a range of 32-token key tiles of one (request b,
-// kv head). Per tile:
+// Attention kernels (split-KV attention and its epilogue). One workgroup = one
+// work unit: a range of 32-token key tiles of one (request b, kv head). Per tile:
 //   - S^T = K Q^T on v_mfma_f32_16x16x32_bf16. Tokens are the M dimension and
 //     the query rows the N dimension, so every lane owns one query row of S^T
-//     and the softmax statistics stay in-lane;
+//     and the softmax statistics stay in-lane (four lanes per row: one quad each);
 //   - online softmax in exp2 space (scores pre-multiplied by sm_scale*log2 e),
 //     masks only on edge tiles; V rows past the sequence end are zeroed by
 //     select, so stale cache slots (even NaN) cannot leak through 0 * NaN;
 //   - O^T += V^T P^T on the same MFMA with P rounded to bf16; the P operand is
 //     exactly the lane's own S^T accumulator registers (no shuffles). V^T comes
 //     from a row-major V tile in LDS through the transposing LDS read.
-// The main loop (stream_kernel) has no workgroup barrier. Each wave owns up to
-// two 16-row blocks of the rows; WR row-waves stream the same tiles (their repeat
-// K/V reads hit L2) and WT token groups stream interleaved tiles of the unit. K
-// goes straight from HBM into the MFMA A fragments; V goes row-major into a
-// private LDS tile. Two tiles are in flight per wave, and the page ids of up to
-// 2048 tiles are staged in LDS once per window, so no scalar load sits on the path.
-// Epilogue: the token groups of the workgroup merge through LDS. A unit that is
-// its request's only split writes the final bf16 output and base-2 LSE itself,
-// and for the windowed form folds in the block keys after each query by the LSE
-// merge (TensorRT-LLM PR #21130, Description item 1 and its formulation table:
-// lse = lse_c (+) lse_f, out = out_c + w (out_f - out_c), w = 2^(lse_f - lse)).
-// Otherwise it writes its fp32 (acc, m, l) partial.
+// Windowed form: row i's keys are its causal window (p - W, p] and the block keys
+// after it, (p, min(N - 1, p + W_r)], all inside the unit's tiles. The block keys
+// after a query are folded into the running softmax state by the online update,
+// which is the log-sum-exp merge of TensorRT-LLM PR #21130 (Description item 1 and
+// its formulation table: lse = lse_c (+) lse_f with out weighted by 2^(lse_c - lse)
+// and 2^(lse_f - lse)) applied tile by tile; with K = 1 or W_r = 0 no later key
+// exists and the causal result is returned as is (item 2).
 //
-// combine_kernel: the LSE combine of the splits and the same merge, one workgroup
-// per output row, launched after the attention kernel. (Combining inside the
-// attention kernel by its last-finishing unit needs an agent-scope release and
-// acquire per unit; on this part those cache write-backs cost far more than a
-// second launch.)
+// stream_kernel (R <= 32): one row-wave, WT token groups per workgroup streaming
+// interleaved tiles, no workgroup barrier in the loop. K goes straight from HBM
+// into the MFMA A fragments; V goes row-major into a private LDS tile. Two tiles
+// are in flight per wave, and the page ids of up to 2048 tiles are staged in LDS
+// once per window, so no scalar load sits on the path.
+// shared_kernel (R > 32): several row-waves consume every tile from an LDS ring
+// the whole workgroup fills (see there).
+// Epilogue: the token groups of the workgroup merge through LDS. A unit that is
+// its request's only split writes the final bf16 output and base-2 LSE itself;
+// otherwise it writes its fp32 (acc, m, l) partial.
+//
+// combine_kernel: the LSE combine of the splits, one workgroup per output row,
+// launched after the attention kernel. (Combining inside the attention kernel by
+// its last-finishing unit needs an agent-scope release and acquire per unit; on
+// this part those cache write-backs cost far more than a second launch.)
 //
 // The split-KV form itself follows the flash-decoding rework of TensorRT-LLM
 // PR #16150 (paged DFlash cross-attention, commits "rework flash-decoding style"
@@ -50,6 +54,16 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int T = kTileTokens;
+
+// LDS row pitches (bf16 elements) of staged K and V tiles, padded against bank
+// conflicts (32 banks of 4 bytes, 128 bytes per cycle). The K fragment read
+// (16 bytes per lane, eight rows per cycle) needs a row stride of an odd multiple
+// of 16 bytes modulo 128: D + 8. The transposing V read (8 bytes per lane, four
+// rows of 32 bytes per 16 lanes) needs a stride of 32 modulo 128: D + 16.
+template <int D>
+constexpr int kKPitch = D + 8;
+template <int D>
+constexpr int kVPitch = D + 16;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -73,6 +87,26 @@ __device__ __forceinline__ u32x4_t ldg16(const uint16_t* p) { return *(const u32
 __device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
     i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p));
     return __builtin_bit_cast(u32x2_t, v);
+}
+
+// Maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the four quads holding one
+// row's tokens), with the gfx950 row-swap permutes: swapping 16-lane rows between
+// two copies of x pairs rows (0,1) and (2,3), swapping 32-lane halves pairs (0,2)
+// and (1,3). VALU only, so no LDS round trip sits in the softmax chain.
+__device__ __forceinline__ float quad_max(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Sum over the same four lanes; every lane gets the same bits ((x0 + x1) + (x2 + x3)
+// in a lane-independent order).
+__device__ __forceinline__ float quad_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float m = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 struct Unit {
@@ -120,6 +154,7 @@ struct WaveRows {
     __device__ __forceinline__ void init(const KernelArgs& a, const Unit& u, int first_block, int lane) {
         const int r16 = lane & 15, quad = lane >> 4;
         const bool left_win = WINDOWED && a.window_left > 0;
+        const int right = a.window_right < 0 ? a.K : a.window_right;  // later block keys a row sees
 #pragma unroll
         for (int n = 0; n < NBW; ++n) {
             const int nb = first_block + n;
@@ -135,14 +170,15 @@ struct WaveRows {
                                                               : u32x4_t{0u, 0u, 0u, 0u});
             const int p = u.C + i;
             row_lo[n] = left_win ? max(0, p - a.window_left + 1) : 0;
-            row_hi[n] = WINDOWED ? p : u.N - 1;
+            // windowed: the causal window and the block keys after the query up to p + W_r
+            row_hi[n] = WINDOWED ? min(u.N - 1, p + right) : u.N - 1;
             m[n] = kNegInf;
             l[n] = 0.f;
 #pragma unroll
             for (int db = 0; db < DB; ++db) acc[n][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
         lo_max = left_win ? max(0, u.C + a.K - a.window_left) : 0;
-        hi_min = WINDOWED ? u.C : u.N - 1;
+        hi_min = WINDOWED ? min(u.N - 1, u.C + right) : u.N - 1;
     }
 
     // Scores of one tile for every owned row block.
@@ -190,8 +226,7 @@ struct WaveRows {
                     }
             }
             float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = quad_max(mx);
             const float mxs = mx * scale;  // scale > 0, so the maximum commutes with it
             if (mxs > m[n] + kRescaleSlack) {
                 const float alpha = fast_exp2(m[n] - mxs);
@@ -219,11 +254,11 @@ struct WaveRows {
 
 // Floats of LDS the epilogue needs (it reuses the tile buffers).
 __host__ __device__ constexpr size_t epilogue_floats(int D, int slots_per_group, int token_groups) {
-    return (size_t)token_groups * slots_per_group * 16 * (D + 4) + 2 * 128 + 128 * kMaxFuture;
+    return (size_t)token_groups * slots_per_group * 16 * (D + 4) + 2 * 128;
 }
 
-// Merge the wave states of a workgroup, then write a partial, or (only split /
-// last arriver) the final bf16 output and LSE, with the windowed merge.
+// Merge the wave states of a workgroup, then write a partial, or (only split)
+// the final bf16 output and LSE.
 template <int D, int NBW, bool WINDOWED, bool ALL_ON>
 __device__ void finish_unit(const KernelArgs& a, const Unit& u, WaveRows<D, NBW, WINDOWED, ALL_ON>& w, int tg,
                             int wr, int WT, int WR, float* lds) {
@@ -235,13 +270,9 @@ __device__ void finish_unit(const KernelArgs& a, const Unit& u, WaveRows<D, NBW,
     float* mg = lds;
     float* rowM = mg + (size_t)WT * slots * 16 * MP;
     float* rowL = rowM + 128;
-    float* sf = rowL + 128;
 
 #pragma unroll
-    for (int n = 0; n < NBW; ++n) {
-        w.l[n] += __shfl_xor(w.l[n], 16);
-        w.l[n] += __shfl_xor(w.l[n], 32);
-    }
+    for (int n = 0; n < NBW; ++n) w.l[n] = quad_sum(w.l[n]);
     __syncthreads();  // tile buffers are free from here on
 #pragma unroll
     for (int n = 0; n < NBW; ++n) {
@@ -293,60 +324,14 @@ __device__ void finish_unit(const KernelArgs& a, const Unit& u, WaveRows<D, NBW,
         return;  // the combine kernel finishes this (request, kv head)
     }
 
-    // Final stage: out = acc / L, lse = M + log2 L, then the future-block-key merge.
-    const int32_t* pt_row = a.page_table + (size_t)u.b * a.stride;
-    if (a.merge) {
-        const int nw = nthreads >> 6, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-        for (int r = wv; r < R; r += nw) {
-            const int i = r / a.g, h = u.hk * a.g + (r - (r / a.g) * a.g);
-            const int p = u.C + i;
-            const int f_hi = a.window_right < 0 ? u.N - 1 : min(u.N - 1, p + a.window_right);
-            const uint16_t* qrow = a.q + ((size_t)(u.b * a.K + i) * a.Hq + h) * D;
-            for (int f = 0; f < f_hi - p; ++f) {
-                const int j = p + 1 + f;
-                const int pid = clampi(pt_row[j / a.P], 0, a.num_pages - 1);
-                const uint16_t* krow = a.kc + (((size_t)pid * a.Hkv + u.hk) * a.P + (j % a.P)) * D;
-                float dot = 0.f;
-                for (int d = lane; d < D; d += 64) dot += bf16_to_f32(qrow[d]) * bf16_to_f32(krow[d]);
-                for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
-                if (lane == 0) sf[r * kMaxFuture + f] = dot * a.scale_log2;
-            }
-        }
-        __syncthreads();
-    }
+    // Final stage: out = acc / L, lse = M + log2 L.
     for (int idx = tid; idx < R * D; idx += nthreads) {
         const int r = idx / D, d = idx - (idx / D) * D;
         const int i = r / a.g, h = u.hk * a.g + (r - (r / a.g) * a.g);
         const float M = rowM[r], L = rowL[r];
-        float o = L > 0.f ? mg[(size_t)r * MP + d] / L : 0.f;
-        float lse = L > 0.f ? M + log2f(L) : kNegInf;
-        if (a.merge) {
-            const int p = u.C + i;
-            const int f_hi = a.window_right < 0 ? u.N - 1 : min(u.N - 1, p + a.window_right);
-            const int nf = f_hi - p;
-            if (nf > 0) {
-                const float* srow = sf + r * kMaxFuture;
-                float mf = kNegInf;
-                for (int f = 0; f < nf; ++f) mf = fmaxf(mf, srow[f]);
-                float z = 0.f;
-                for (int f = 0; f < nf; ++f) z += fast_exp2(srow[f] - mf);
-                const float lse_f = mf + log2f(z);
-                float of = 0.f;
-                for (int f = 0; f < nf; ++f) {
-                    const int j = p + 1 + f;
-                    const int pid = clampi(pt_row[j / a.P], 0, a.num_pages - 1);
-                    of += fast_exp2(srow[f] - lse_f) *
-                          bf16_to_f32(a.vc[(((size_t)pid * a.Hkv + u.hk) * a.P + (j % a.P)) * D + d]);
-                }
-                const float hi2 = fmaxf(lse, lse_f), lo2 = fminf(lse, lse_f);
-                const float merged = hi2 + log2f(1.f + fast_exp2(lo2 - hi2));
-                o = o + fast_exp2(lse_f - merged) * (of - o);
-                lse = merged;
-            }
-        }
         const size_t orow = (size_t)(u.b * a.K + i) * a.Hq + h;
-        a.out[orow * D + d] = f32_to_bf16_rne(o);
-        if (d == 0 && a.lse) a.lse[orow] = lse;
+        a.out[orow * D + d] = f32_to_bf16_rne(L > 0.f ? mg[(size_t)r * MP + d] / L : 0.f);
+        if (d == 0 && a.lse) a.lse[orow] = L > 0.f ? M + log2f(L) : kNegInf;
     }
 }
 
@@ -362,7 +347,7 @@ template <int D, int NBW, bool WINDOWED, bool ALL_ON, int MAXT>
 __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
     constexpr int KK = D / 32, DB = D / 16;
     constexpr int VCH = D / 16;   // 1-KiB chunks of the V tile (16 bytes per lane each)
-    constexpr int VP = D + 8;     // padded row pitch of the V tile in LDS (bf16 elements)
+    constexpr int VP = kVPitch<D>;  // padded row pitch of the V tile in LDS (bf16 elements)
     constexpr int RPC = 512 / D;  // tile rows per chunk
 
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -494,7 +479,168 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
 }
 
 // ---------------------------------------------------------------------------------
-// Separate combine (+ merge) of the splits: one workgroup per output row.
+// Shared-tile main loop for many query rows (R > 32): WR row-waves, each owning up
+// to NBW row blocks, all consume every tile of the unit. Where each row-wave loading
+// its own copy of a tile would leave only about one tile of unique bytes in flight
+// per workgroup, here the workgroup loads each tile once: each wave moves LPT
+// 1-KiB blocks of K and V (16 bytes per lane), DR tiles ahead of the one being
+// consumed, into a two-slot LDS ring (row-major, padded pitch). One workgroup
+// barrier per tile orders the ring; it waits on LDS traffic only, so the DR tiles
+// of global loads stay in flight across it. Loads sit at fixed places (the tile
+// index is clamped past the unit's end), so each wait names exactly one tile.
+template <int D, int NBW, bool WINDOWED, bool ALL_ON, int WR, int DR>
+__global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared_kernel(const KernelArgs a) {
+    constexpr int NT = 64 * WR;
+    constexpr int P8 = D / 8;             // 16-byte pieces per tile row
+    constexpr int NBLK = D / 8;           // 1-KiB blocks per tile (64 pieces each): K and V, 32 rows
+    constexpr int BP = NBLK / 4;          // blocks per 16-row half of K or V
+    constexpr int RPB = 512 / D;          // tile rows per block
+    constexpr int LPT = (NBLK + WR - 1) / WR;
+    constexpr int KP = kKPitch<D>;        // padded row pitch (bf16) of the K tile in LDS
+    constexpr int VP = kVPitch<D>;        // and of the V tile
+    constexpr int SLOT = T * (KP + VP);   // bf16 elements per ring slot: K tile, then V tile
+    constexpr int DB = D / 16, KK = D / 32;
+
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15, quad = lane >> 4;
+    const Unit u = decode_unit<WINDOWED>(a);
+    WaveRows<D, NBW, WINDOWED, ALL_ON> w;
+    w.init(a, u, wave * NBW, lane);
+    int* pid_tab = reinterpret_cast<int*>(lds + 2 * SLOT);
+
+    const int32_t* pt_row = a.page_table + (size_t)u.b * a.stride;
+    const int last_page = (u.N - 1) / a.P;
+    const size_t head_elems = (size_t)a.P * D;
+    // This lane's piece inside any block: row lrow of the block, columns lcol..lcol+7.
+    const int lrow = lane / P8, lcol = (lane % P8) * 8;
+    const uint32_t lane_goff = (uint32_t)(lrow * D + lcol) * 2;   // bytes, in the cache
+    const uint32_t lane_koff = (uint32_t)(lrow * KP + lcol) * 2;  // bytes, in the K tile
+    const uint32_t lane_voff = (uint32_t)(lrow * VP + lcol) * 2;  // bytes, in the V tile
+
+    struct Stage {
+        u32x4_t c[LPT];
+    };
+
+    for (int win = u.ulo; win < u.uhi; win += kPidWindow) {
+        const int span = min(u.uhi - win, kPidWindow);
+        __syncthreads();  // the previous window is done with the page-id table and the ring
+        {
+            // entry 2j + h: page of half h (16 tokens) of tile win + j
+            const int n = 2 * span;
+            for (int j0 = 0; j0 < n; j0 += 8 * NT) {
+                int v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int j = j0 + e * NT + tid;
+                    const int tok = (win + (j >> 1)) * T + 16 * (j & 1);
+                    v[e] = j < n ? pt_row[min(tok / a.P, last_page)] : 0;
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int j = j0 + e * NT + tid;
+                    if (j < n) pid_tab[j] = clampi(v[e], 0, a.num_pages - 1);
+                }
+            }
+        }
+        __syncthreads();
+        const int nk = span;
+
+        // A tile is NBLK blocks of 64 16-byte pieces in four parts (K rows 0-15,
+        // K rows 16-31, V rows 0-15, V rows 16-31) of BP blocks each. Wave w moves
+        // blocks w, w + WR, ... (clamped: a wave past the last block repeats it, writing
+        // the same bytes to the same place), so each block's part, page and bases are
+        // wave-uniform scalars and a lane's offset inside a block is fixed.
+        auto issue = [&](Stage& st, int t) {
+            const int tc = min(t, nk - 1);
+            const int pid0 = __builtin_amdgcn_readfirstlane(pid_tab[2 * tc]);
+            const int pid1 = __builtin_amdgcn_readfirstlane(pid_tab[2 * tc + 1]);
+            const int t0 = (win + tc) * T;
+            const size_t slab0 = ((size_t)pid0 * a.Hkv + u.hk) * head_elems + (size_t)(t0 % a.P) * D;
+            const size_t slab1 = ((size_t)pid1 * a.Hkv + u.hk) * head_elems + (size_t)((t0 + 16) % a.P) * D;
+#pragma unroll
+            for (int k = 0; k < LPT; ++k) {
+                const int b = min(wave + k * WR, NBLK - 1);
+                const int part = b / BP;
+                const uint16_t* base = ((part >> 1) ? a.vc : a.kc) + ((part & 1) ? slab1 : slab0) + (b % BP) * RPB * D;
+                st.c[k] = *(const u32x4_t*)(reinterpret_cast<const char*>(base) + lane_goff);
+            }
+        };
+        auto store = [&](const Stage& st, int t, int slot) {
+            const int t0 = (win + t) * T;
+            const bool tail = t0 + T > u.N;
+            char* dst = reinterpret_cast<char*>(lds + slot * SLOT);
+#pragma unroll
+            for (int k = 0; k < LPT; ++k) {
+                const int b = min(wave + k * WR, NBLK - 1);
+                const int part = b / BP;
+                const int row0 = (part & 1) * 16 + (b % BP) * RPB;  // first tile row of the block
+                u32x4_t v = st.c[k];
+                if (part >> 1) {
+                    // V rows past the sequence end become zeros (stale slots may hold NaN)
+                    if (tail && t0 + row0 + lrow >= u.N) v = u32x4_t{0u, 0u, 0u, 0u};
+                    *(u32x4_t*)(dst + (T * KP + row0 * VP) * 2 + lane_voff) = v;
+                } else {
+                    *(u32x4_t*)(dst + row0 * KP * 2 + lane_koff) = v;
+                }
+            }
+        };
+        auto compute = [&](int t, int slot) {
+            const int t0 = (win + t) * T;
+            const uint16_t* kl = lds + slot * SLOT;
+            const uint16_t* vl = kl + T * KP;
+            bf16x8_t kf[2][KK];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk)
+                    kf[mb][kk] = __builtin_bit_cast(
+                        bf16x8_t, *(const u32x4_t*)(kl + (mb * 16 + r16) * KP + kk * 32 + quad * 8));
+            f32x4_t s[NBW][2];
+            w.scores(kf, s);
+            bf16x8_t vf[DB];
+            const uint16_t* vrow = vl + (4 * quad + (r16 >> 2)) * VP + 4 * (r16 & 3);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const u32x2_t lo = lds_read_tr16(vrow + db * 16);
+                const u32x2_t hi = lds_read_tr16(vrow + 16 * VP + db * 16);
+                vf[db] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+            }
+            w.update(s, vf, t0, a.scale_log2, quad);
+        };
+
+        // Tile t waits in st[t % DR] until it is written to ring slot t & 1. The
+        // scheduling barriers keep the loads of successive tiles in tile order, so the
+        // counter wait before each store covers exactly the oldest tile.
+        Stage st[DR];
+#pragma unroll
+        for (int j = 0; j < DR; ++j) {
+            issue(st[j], j);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        store(st[0], 0, 0);
+        issue(st[0], DR);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        for (int tb = 0; tb < nk; tb += DR) {
+#pragma unroll
+            for (int j = 0; j < DR; ++j) {
+                const int t = tb + j;
+                if (t < nk) compute(t, t & 1);
+                store(st[(j + 1) % DR], t + 1, (t + 1) & 1);
+                issue(st[(j + 1) % DR], t + 1 + DR);
+                __builtin_amdgcn_sched_barrier(0);
+                __syncthreads();
+            }
+        }
+    }
+    finish_unit(a, u, w, 0, wave, 1, WR, reinterpret_cast<float*>(lds));
+}
+
+// ---------------------------------------------------------------------------------
+// LSE combine of the splits: one workgroup per output row.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const KernelArgs a) {
     constexpr int DL = D / 4;     // threads per split row, 4 floats each
@@ -502,8 +648,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const KernelArgs a) {
     __shared__ float red_acc[SL][D];
     __shared__ float red_l[SL];
     __shared__ float red_m[4];
-    __shared__ float o_c[D];
-    __shared__ float s_f[kMaxFuture];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = blockIdx.x;
@@ -542,55 +686,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const KernelArgs a) {
     if (tid < D) {
         float o = 0.f;
         for (int k = 0; k < SL; ++k) o += red_acc[k][tid];
-        o_c[tid] = L > 0.f ? o / L : 0.f;
+        a.out[orow * D + tid] = f32_to_bf16_rne(L > 0.f ? o / L : 0.f);
     }
-    float lse = L > 0.f ? M + log2f(L) : kNegInf;
-    __syncthreads();
-
-    if (a.merge) {
-        const int N = clampi(a.seq_lens[b], a.K, a.stride * a.P);
-        const int p = N - a.K + i;
-        const int f_hi = a.window_right < 0 ? N - 1 : min(N - 1, p + a.window_right);
-        const int nf = f_hi - p;
-        if (nf > 0) {
-            const int32_t* pt_row = a.page_table + (size_t)b * a.stride;
-            const uint16_t* qrow = a.q + orow * D;
-            if (wave == 0) {
-                for (int f = 0; f < nf; ++f) {
-                    const int j = p + 1 + f;
-                    const int pid = clampi(pt_row[j / a.P], 0, a.num_pages - 1);
-                    const uint16_t* krow = a.kc + (((size_t)pid * a.Hkv + hk) * a.P + (j % a.P)) * D;
-                    float dot = 0.f;
-                    for (int d = lane; d < D; d += 64) dot += bf16_to_f32(qrow[d]) * bf16_to_f32(krow[d]);
-                    for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
-                    if (lane == 0) s_f[f] = dot * a.scale_log2;
-                }
-            }
-            __syncthreads();
-            float mf = kNegInf;
-            for (int f = 0; f < nf; ++f) mf = fmaxf(mf, s_f[f]);
-            float z = 0.f;
-            for (int f = 0; f < nf; ++f) z += fast_exp2(s_f[f] - mf);
-            const float lse_f = mf + log2f(z);
-            const float hi2 = fmaxf(lse, lse_f), lo2 = fminf(lse, lse_f);
-            const float merged = hi2 + log2f(1.f + fast_exp2(lo2 - hi2));
-            const float wf = fast_exp2(lse_f - merged);
-            if (tid < D) {
-                float of = 0.f;
-                for (int f = 0; f < nf; ++f) {
-                    const int j = p + 1 + f;
-                    const int pid = clampi(pt_row[j / a.P], 0, a.num_pages - 1);
-                    of += fast_exp2(s_f[f] - lse_f) *
-                          bf16_to_f32(a.vc[(((size_t)pid * a.Hkv + hk) * a.P + (j % a.P)) * D + tid]);
-                }
-                o_c[tid] = o_c[tid] + wf * (of - o_c[tid]);
-            }
-            lse = merged;
-            __syncthreads();
-        }
-    }
-    if (tid < D) a.out[orow * D + tid] = f32_to_bf16_rne(o_c[tid]);
-    if (tid == 0 && a.lse) a.lse[orow] = lse;
+    if (tid == 0 && a.lse) a.lse[orow] = L > 0.f ? M + log2f(L) : kNegInf;
 }
 
 template <typename F>
@@ -613,8 +711,46 @@ hipError_t launch_stream(const KernelShape& s, int units, const KernelArgs& args
                            s.lds_bytes, args, stream, &granted);
 }
 
+// Tiles in flight per lane: about 96 registers of staged loads for a wave alone on
+// its SIMD (D = 128, two row blocks), 64 where two waves share a SIMD, at most 8.
+constexpr int shared_depth(int D, int NBW, int WR) {
+    const int lpt = (D / 8 + WR - 1) / WR;  // 1-KiB blocks per wave per tile
+    const int dr = ((D == 128 && NBW == 2) ? 24 : 16) / lpt;
+    return dr < 2 ? 2 : (dr > 8 ? 8 : dr);
+}
+
+template <int D, int NBW, int WR, bool W, bool ALL_ON>
+hipError_t launch_shared(const KernelShape& s, int units, const KernelArgs& args, hipStream_t stream) {
+    static size_t granted = 0;
+    return launch_with_lds(shared_kernel<D, NBW, W, ALL_ON, WR, shared_depth(D, NBW, WR)>, units, 64 * WR,
+                           s.lds_bytes, args, stream, &granted);
+}
+
 template <bool W>
 hipError_t dispatch(const KernelShape& s, int units, const KernelArgs& args, hipStream_t stream) {
+    if (s.shared) {
+#define BA_SHARED(D_, NBW_, WR_)                                                                        \
+    if (s.head_dim == D_ && s.nbw == NBW_ && s.row_waves == WR_)                                        \
+        return s.all_on ? launch_shared<D_, NBW_, WR_, W, true>(s, units, args, stream)                 \
+                        : launch_shared<D_, NBW_, WR_, W, false>(s, units, args, stream);
+#define BA_SHARED1(D_, WR_)                                                                             \
+    if (s.head_dim == D_ && s.nbw == 1 && s.row_waves == WR_) return launch_shared<D_, 1, WR_, W, true>(s, units, args, stream);
+        BA_SHARED(64, 2, 2)
+        BA_SHARED(64, 2, 3)
+        BA_SHARED(64, 2, 4)
+        BA_SHARED(128, 2, 2)
+        BA_SHARED(128, 2, 3)
+        BA_SHARED(128, 2, 4)
+        BA_SHARED1(128, 3)
+        BA_SHARED1(128, 4)
+        BA_SHARED1(128, 5)
+        BA_SHARED1(128, 6)
+        BA_SHARED1(128, 7)
+        BA_SHARED1(128, 8)
+#undef BA_SHARED
+#undef BA_SHARED1
+        return hipErrorInvalidValue;
+    }
 #define BA_CASE(D_, NBW_)                                                                               \
     if (s.head_dim == D_ && s.nbw == NBW_)                                                              \
         return s.all_on ? launch_stream<D_, NBW_, W, true>(s, units, args, stream)                      \
@@ -632,7 +768,14 @@ hipError_t dispatch(const KernelShape& s, int units, const KernelArgs& args, hip
 size_t attention_lds_bytes(const KernelShape& s, int R) {
     (void)R;
     const int D = s.head_dim;
-    const size_t loop = ((size_t)s.token_groups * s.row_waves * kTileTokens) * (D + 8) * sizeof(uint16_t) +
+    if (s.shared) {
+        const size_t pitches = D == 64 ? kKPitch<64> + kVPitch<64> : kKPitch<128> + kVPitch<128>;
+        const size_t ring = (size_t)2 * kTileTokens * pitches * sizeof(uint16_t) + 2 * kPidWindow * sizeof(int);
+        const size_t epi = epilogue_floats(D, s.row_waves * s.nbw, 1) * sizeof(float);
+        return ring > epi ? ring : epi;
+    }
+    const size_t vpitch = D == 64 ? kVPitch<64> : kVPitch<128>;
+    const size_t loop = ((size_t)s.token_groups * s.row_waves * kTileTokens) * vpitch * sizeof(uint16_t) +
                         2 * kPidWindow * sizeof(int);
     const size_t epi = epilogue_floats(D, s.row_waves * s.nbw, s.token_groups) * sizeof(float);
     return loop > epi ? loop : epi;

@@ -66,8 +66,26 @@ def test_waves_override():
     assert plan_info(params(waves_override=8), [5000, 5000])["token_groups"] == 8
     assert plan_info(params(waves_override=1), [5000, 5000])["waves_per_unit"] == 1
     w = dict(head_dim=128, page_size=64, num_q_heads=16, num_kv_heads=1, window_left=4096, block_size=7)
+    # R = 112 at D = 128 shares tiles: waves per workgroup = rows per wave choice
     info = plan_info(params(**w, waves_override=8), [8199, 8199])
-    assert info["row_waves"] == 4 and info["token_groups"] == 1
+    assert info["row_waves"] == 7 and info["token_groups"] == 1 and info["shared_tiles"] == 1
+    info = plan_info(params(**w, waves_override=4), [8199, 8199])
+    assert info["row_waves"] == 4 and info["waves_per_unit"] == 4
+    info = plan_info(params(**w, waves_override=1), [8199, 8199])
+    assert info["row_waves"] == 4  # at most two row blocks per wave
+
+
+def test_tile_kernel_choice():
+    # R <= 32: one row-wave, waves stream their own tiles; more rows share tiles through LDS
+    assert plan_info(params(), [5000, 5000])["shared_tiles"] == 0
+    info = plan_info(params(num_q_heads=16, num_kv_heads=1, block_size=3), [5000, 5000])  # R = 48, D = 64
+    assert info["shared_tiles"] == 1 and info["row_waves"] == 2 and info["waves_per_unit"] == 2
+    w = dict(head_dim=128, page_size=64, num_q_heads=16, num_kv_heads=1, window_left=4096)
+    info = plan_info(params(**w, block_size=5), [8197, 8197])  # R = 80: one row block per wave
+    assert info["shared_tiles"] == 1 and info["row_waves"] == 5 and info["token_groups"] == 1
+    info = plan_info(params(**w, block_size=3), [8195, 8195])  # R = 48: two blocks per wave
+    assert info["shared_tiles"] == 1 and info["row_waves"] == 2
+    assert plan_info(params(**w, block_size=1), [8193, 8193])["shared_tiles"] == 0  # R = 16
 
 
 def test_splits_override_and_clamp():
@@ -83,7 +101,7 @@ def test_windowed_plan_merge_flag():
     assert plan_info(params(**w, block_size=1, window_right=-1), [8193, 8193])["merge_active"] == 0
     assert plan_info(params(**w, block_size=7, window_right=0), [8199, 8199])["merge_active"] == 0
     info = plan_info(params(**w, block_size=7, window_right=-1), [8199, 8199])
-    assert info["kind"] == 1 and info["row_waves"] == 4
+    assert info["kind"] == 1 and info["row_waves"] == 7
 
 
 @pytest.mark.parametrize("B", [1, 2, 32, 33, 200])

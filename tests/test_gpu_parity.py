@@ -51,6 +51,9 @@ SMALL = [
     (7, dict(batch=2, K=3, hq=16, hkv=1, D=128, P=64, ctx=2100)),     # R = 48
     (8, dict(batch=2, K=7, hq=16, hkv=1, D=128, P=128, ctx=950)),     # R = 112, P = 128
     (9, dict(batch=2, K=7, hq=8, hkv=2, D=64, P=32, ctx=4096)),       # page-aligned end
+    (10, dict(batch=2, K=5, hq=16, hkv=1, D=128, P=16, ctx=1500)),    # R = 80: three row-waves, 16-token pages
+    (11, dict(batch=3, K=3, hq=16, hkv=1, D=64, P=16, ctx_range=(30, 700))),  # R = 48 on D = 64, mixed lengths
+    (12, dict(batch=1, K=8, hq=16, hkv=1, D=128, P=32, ctx=2222)),    # R = 128: every row block live
 ]
 
 
@@ -65,6 +68,8 @@ WSMALL = [
     (23, dict(batch=2, K=7, hq=8, hkv=2, D=64, P=32, ctx=500, wl=33, wr=2)),
     (24, dict(batch=2, K=3, hq=16, hkv=1, D=128, P=64, ctx=10, wl=4096, wr=-1)),  # window longer than cache
     (25, dict(batch=2, K=7, hq=16, hkv=1, D=128, P=64, ctx=700, wl=1, wr=-1)),    # self + later keys only
+    (26, dict(batch=2, K=5, hq=16, hkv=1, D=128, P=64, ctx=5000, wl=4096, wr=-1)),  # R = 80, window inside
+    (27, dict(batch=3, K=7, hq=16, hkv=1, D=64, P=32, ctx_range=(10, 2000), wl=100, wr=3)),  # R = 112, D = 64
 ]
 
 
@@ -87,6 +92,30 @@ def test_split_invariance(splits):
     base, base_lse, _ = H.run(dc, splits=1)
     # different split counts only reorder fp32 sums: agreement well inside the parity bar
     assert np.abs(out - base).max() <= 4 * H.ulp_bf16(float(np.abs(base).max()))
+
+
+@pytest.mark.parametrize("splits", [1, 3, 1000])
+def test_split_invariance_shared_tiles(splits):
+    c = case(36, batch=2, K=7, hq=16, hkv=1, D=128, P=64, ctx=3000, wl=2000, wr=-1)
+    inp = synth.make_inputs(c)
+    dc = H.upload(inp)
+    ref_out, ref_lse = oracle.attention_case(inp)
+    out, lse, info = H.run(dc, splits=splits)
+    assert info["shared_tiles"] == 1 and info["row_waves"] == 7
+    H.compare(out, lse, ref_out, ref_lse, label=f"shared splits={splits}")
+    base, _, _ = H.run(dc, splits=1)
+    assert np.abs(out - base).max() <= 4 * H.ulp_bf16(float(np.abs(base).max()))
+
+
+@pytest.mark.parametrize("K,waves,row_waves", [(7, 4, 4), (5, 3, 3), (3, 3, 3), (7, 8, 7)])
+def test_rows_per_wave_variants(K, waves, row_waves):
+    """Every row-blocks-per-wave choice of the shared-tile kernel at D = 128 meets the bar."""
+    c = case(37 + K, batch=2, K=K, hq=16, hkv=1, D=128, P=64, ctx=2500, wl=1000, wr=-1)
+    inp = synth.make_inputs(c)
+    ref_out, ref_lse = oracle.attention_case(inp)
+    out, lse, info = H.run(H.upload(inp), waves=waves)
+    assert info["shared_tiles"] == 1 and info["row_waves"] == row_waves
+    H.compare(out, lse, ref_out, ref_lse, label=f"K={K} waves={waves}")
 
 
 def test_empty_splits_from_shorter_live_lengths():
