@@ -89,6 +89,8 @@ int validate(const blockattn_params* p, const int32_t* lens) {
                     "block_size * (num_q_heads / num_kv_heads) must be <= 128 query rows per kv head");
     if (p->page_table_stride < 1) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "page_table_stride must be >= 1");
     if (p->num_pages < 1) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "num_pages must be >= 1");
+    if ((int64_t)p->num_pages * p->num_kv_heads > INT32_MAX)
+        return fail(BLOCKATTN_ERR_UNSUPPORTED, "num_pages * num_kv_heads must stay below 2^31 (pool slabs are int32)");
     if (!(std::isfinite(p->sm_scale) && p->sm_scale > 0.f))
         return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "sm_scale must be finite and > 0");
     if (p->window_left == 0 || p->window_left < -1)
@@ -295,6 +297,7 @@ int run_forward(blockattn_plan_t plan, const void* q, const void* k, const void*
     ka.g = plan->g;
     ka.R = plan->R;
     ka.P = p.page_size;
+    ka.p_shift = __builtin_ctz((unsigned)p.page_size);
     ka.stride = p.page_table_stride;
     ka.num_pages = p.num_pages;
     ka.window_left = p.window_left;

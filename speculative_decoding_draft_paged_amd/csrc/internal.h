@@ -32,6 +32,7 @@ struct KernelArgs {
     uint16_t* out;
     float* lse;
     int32_t K, Hq, Hkv, g, R, P, stride, num_pages;
+    int32_t p_shift;       // log2 P
     int32_t window_left;   // -1: none
     int32_t window_right;  // -1: every later block key
     int32_t row_waves;     // WR: waves streaming the same tiles, each owning NBW row blocks

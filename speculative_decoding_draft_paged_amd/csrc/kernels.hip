@@ -54,14 +54,18 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int T = kTileTokens;
-
-// LDS row pitches (bf16 elements) of staged K and V tiles, padded against bank
-// conflicts (32 banks of 4 bytes, 128 bytes per cycle). The K fragment read
-// (16 bytes per lane, eight rows per cycle) needs a row stride of an odd multiple
-// of 16 bytes modulo 128: D + 8. The transposing V read (8 bytes per lane, four
-// rows of 32 bytes per 16 lanes) needs a stride of 32 modulo 128: D + 16.
 template <int D>
-constexpr int kKPitch = D + 8;
+constexpr int kLog2 = D == 64 ? 6 : 7;
+
+// LDS row pitches (bf16 elements) of staged K and V tiles. Both reads of a tile
+// move 256 bytes per cycle: the K fragment read (16 bytes per lane; lanes of eight
+// rows in two column groups served together) and the transposing V read (8 bytes
+// per lane; eight rows of 32 bytes together). Measured on gfx950, a row stride of 32
+// modulo 256 bytes is free of bank conflicts for both (16, 48, 64 or 80 give
+// two-way conflicts, 0 eight-way), and the rule only needs an odd multiple of 32
+// bytes, which D + 16 elements gives for D = 64 (160 bytes) and 128 (288 bytes).
+template <int D>
+constexpr int kKPitch = D + 16;
 template <int D>
 constexpr int kVPitch = D + 16;
 
@@ -365,8 +369,8 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
     int* pid_tab = reinterpret_cast<int*>(lds + (size_t)WT * WR * T * VP);
 
     const int32_t* pt_row = a.page_table + (size_t)u.b * a.stride;
-    const int last_page = (u.N - 1) / a.P;
-    const size_t head_elems = (size_t)a.P * D;
+    const int last_page = (u.N - 1) >> a.p_shift;
+    const int pmask = (1 << a.p_shift) - 1;
 
     struct TileRegs {
         u32x4_t k[2][KK];
@@ -377,7 +381,7 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
         const int span = min(u.uhi - win, kPidWindow);
         __syncthreads();  // the previous window is done with the page-id table
         {
-            // entry 2j + h: page of half h (16 tokens) of tile win + j
+            // entry 2j + h: slab (page * Hkv + kv head) of half h (16 tokens) of tile win + j
             const int n = 2 * span;
             for (int j0 = 0; j0 < n; j0 += 8 * nthreads) {
                 int v[8];
@@ -385,12 +389,12 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
                 for (int e = 0; e < 8; ++e) {
                     const int j = j0 + e * nthreads + tid;
                     const int tok = (win + (j >> 1)) * T + 16 * (j & 1);
-                    v[e] = j < n ? pt_row[min(tok / a.P, last_page)] : 0;
+                    v[e] = j < n ? pt_row[min(tok >> a.p_shift, last_page)] : 0;
                 }
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int j = j0 + e * nthreads + tid;
-                    if (j < n) pid_tab[j] = clampi(v[e], 0, a.num_pages - 1);
+                    if (j < n) pid_tab[j] = clampi(v[e], 0, a.num_pages - 1) * a.Hkv + u.hk;
                 }
             }
         }
@@ -401,10 +405,11 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
         auto issue = [&](TileRegs& t, int k) {
             const int kc = min(k, nk - 1);
             const int j = 2 * (tg + kc * WT);
-            const int pid0 = pid_tab[j], pid1 = pid_tab[j + 1];
+            const int slab0 = __builtin_amdgcn_readfirstlane(pid_tab[j]);
+            const int slab1 = __builtin_amdgcn_readfirstlane(pid_tab[j + 1]);
             const int t0 = (win + tg + kc * WT) * T;
-            const size_t base0 = ((size_t)pid0 * a.Hkv + u.hk) * head_elems + (size_t)(t0 % a.P) * D;
-            const size_t base1 = ((size_t)pid1 * a.Hkv + u.hk) * head_elems + (size_t)((t0 + 16) % a.P) * D;
+            const size_t base0 = ((size_t)slab0 << (a.p_shift + kLog2<D>)) + (size_t)((t0 & pmask) * D);
+            const size_t base1 = ((size_t)slab1 << (a.p_shift + kLog2<D>)) + (size_t)(((t0 + 16) & pmask) * D);
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -512,8 +517,8 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
     int* pid_tab = reinterpret_cast<int*>(lds + 2 * SLOT);
 
     const int32_t* pt_row = a.page_table + (size_t)u.b * a.stride;
-    const int last_page = (u.N - 1) / a.P;
-    const size_t head_elems = (size_t)a.P * D;
+    const int last_page = (u.N - 1) >> a.p_shift;
+    const int pmask = (1 << a.p_shift) - 1;
     // This lane's piece inside any block: row lrow of the block, columns lcol..lcol+7.
     const int lrow = lane / P8, lcol = (lane % P8) * 8;
     const uint32_t lane_goff = (uint32_t)(lrow * D + lcol) * 2;   // bytes, in the cache
@@ -528,7 +533,7 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
         const int span = min(u.uhi - win, kPidWindow);
         __syncthreads();  // the previous window is done with the page-id table and the ring
         {
-            // entry 2j + h: page of half h (16 tokens) of tile win + j
+            // entry 2j + h: slab (page * Hkv + kv head) of half h (16 tokens) of tile win + j
             const int n = 2 * span;
             for (int j0 = 0; j0 < n; j0 += 8 * NT) {
                 int v[8];
@@ -536,12 +541,12 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
                 for (int e = 0; e < 8; ++e) {
                     const int j = j0 + e * NT + tid;
                     const int tok = (win + (j >> 1)) * T + 16 * (j & 1);
-                    v[e] = j < n ? pt_row[min(tok / a.P, last_page)] : 0;
+                    v[e] = j < n ? pt_row[min(tok >> a.p_shift, last_page)] : 0;
                 }
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int j = j0 + e * NT + tid;
-                    if (j < n) pid_tab[j] = clampi(v[e], 0, a.num_pages - 1);
+                    if (j < n) pid_tab[j] = clampi(v[e], 0, a.num_pages - 1) * a.Hkv + u.hk;
                 }
             }
         }
@@ -555,11 +560,11 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
         // wave-uniform scalars and a lane's offset inside a block is fixed.
         auto issue = [&](Stage& st, int t) {
             const int tc = min(t, nk - 1);
-            const int pid0 = __builtin_amdgcn_readfirstlane(pid_tab[2 * tc]);
-            const int pid1 = __builtin_amdgcn_readfirstlane(pid_tab[2 * tc + 1]);
+            const int sl0 = __builtin_amdgcn_readfirstlane(pid_tab[2 * tc]);
+            const int sl1 = __builtin_amdgcn_readfirstlane(pid_tab[2 * tc + 1]);
             const int t0 = (win + tc) * T;
-            const size_t slab0 = ((size_t)pid0 * a.Hkv + u.hk) * head_elems + (size_t)(t0 % a.P) * D;
-            const size_t slab1 = ((size_t)pid1 * a.Hkv + u.hk) * head_elems + (size_t)((t0 + 16) % a.P) * D;
+            const size_t slab0 = ((size_t)sl0 << (a.p_shift + kLog2<D>)) + (size_t)((t0 & pmask) * D);
+            const size_t slab1 = ((size_t)sl1 << (a.p_shift + kLog2<D>)) + (size_t)(((t0 + 16) & pmask) * D);
 #pragma unroll
             for (int k = 0; k < LPT; ++k) {
                 const int b = min(wave + k * WR, NBLK - 1);

@@ -116,6 +116,7 @@ def test_workspace_size_grows_with_batch(B):
 
 @pytest.mark.parametrize("kw,lens,code,needle", [
     (dict(head_dim=96), [100, 100], ba.BLOCKATTN_ERR_UNSUPPORTED, "head_dim"),
+    (dict(num_pages=2 ** 30), [100, 100], ba.BLOCKATTN_ERR_UNSUPPORTED, "num_pages * num_kv_heads"),
     (dict(page_size=48), [100, 100], ba.BLOCKATTN_ERR_UNSUPPORTED, "page_size"),
     (dict(num_q_heads=7), [100, 100], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "num_q_heads"),
     (dict(block_size=17), [100, 100], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "block_size"),
