@@ -256,86 +256,120 @@ struct WaveRows {
     }
 };
 
-// Floats of LDS the epilogue needs (it reuses the tile buffers).
+// Floats of LDS the epilogue needs (it reuses the tile buffers): per token group
+// and row the (m, l) pair, and the scaled accumulators of token groups 1..WT-1
+// (row pitch D + 8 floats: an odd multiple of 32 bytes, free of bank conflicts).
 __host__ __device__ constexpr size_t epilogue_floats(int D, int slots_per_group, int token_groups) {
-    return (size_t)token_groups * slots_per_group * 16 * (D + 4) + 2 * 128;
+    return token_groups <= 1 ? 0
+                             : (size_t)token_groups * slots_per_group * 16 * 2 +
+                                   (size_t)(token_groups - 1) * slots_per_group * 16 * (D + 8);
 }
 
-// Merge the wave states of a workgroup, then write a partial, or (only split)
-// the final bf16 output and LSE.
+// Store one wave's rows: acc holds O^T fragments (lane: query row r16 of block n,
+// dims db*16 + 4*quad .. +3), already scaled to the row's final weights when
+// `final`, else relative to 2^m. m, l: the row's reference maximum (log2 units)
+// and weight sum.
+template <int D>
+__device__ __forceinline__ void store_rows(const KernelArgs& a, const Unit& u, int r, bool final, const f32x4_t (&acc)[D / 16],
+                                           float m, float l, int quad) {
+    constexpr int DB = D / 16;
+    if (r >= a.R) return;
+    if (!final) {
+        const size_t pr = (size_t)blockIdx.x * a.R + r;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) *(f32x4_t*)(a.part_acc + pr * D + db * 16 + quad * 4) = acc[db];
+        if (quad == 0) {
+            a.part_m[pr] = m;
+            a.part_l[pr] = l;
+        }
+        return;
+    }
+    const int i = r / a.g, h = u.hk * a.g + (r - (r / a.g) * a.g);
+    const size_t orow = (size_t)(u.b * a.K + i) * a.Hq + h;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        const uint32_t lo = f32_to_bf16_rne(acc[db][0]) | ((uint32_t)f32_to_bf16_rne(acc[db][1]) << 16);
+        const uint32_t hi = f32_to_bf16_rne(acc[db][2]) | ((uint32_t)f32_to_bf16_rne(acc[db][3]) << 16);
+        *(u32x2_t*)(a.out + orow * D + db * 16 + quad * 4) = u32x2_t{lo, hi};
+    }
+    if (quad == 0 && a.lse) a.lse[orow] = l > 0.f ? m + log2f(l) : kNegInf;
+}
+
+// Epilogue of a unit: merge the token groups' softmax states, then write the
+// unit's partial (a split request) or the final bf16 output and base-2 LSE.
+// With one token group every wave owns whole rows and stores from registers.
 template <int D, int NBW, bool WINDOWED, bool ALL_ON>
 __device__ void finish_unit(const KernelArgs& a, const Unit& u, WaveRows<D, NBW, WINDOWED, ALL_ON>& w, int tg,
                             int wr, int WT, int WR, float* lds) {
-    constexpr int DB = D / 16, MP = D + 4;
-    const int tid = threadIdx.x, nthreads = blockDim.x;
+    constexpr int DB = D / 16, XP = D + 8;
+    const int tid = threadIdx.x;
     const int lane = tid & 63, r16 = lane & 15, quad = lane >> 4;
-    const int R = a.R;
-    const int slots = WR * NBW;
-    float* mg = lds;
-    float* rowM = mg + (size_t)WT * slots * 16 * MP;
-    float* rowL = rowM + 128;
+    const int slots = WR * NBW;  // row blocks per token group
+    const bool final = u.S <= 1;
 
 #pragma unroll
     for (int n = 0; n < NBW; ++n) w.l[n] = quad_sum(w.l[n]);
+
+    if (WT == 1) {
+#pragma unroll
+        for (int n = 0; n < NBW; ++n) {
+            if (!ALL_ON && !w.on[n]) continue;
+            const float l = w.l[n];
+            const float inv = final && l > 0.f ? 1.f / l : (final ? 0.f : 1.f);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) w.acc[n][db] *= inv;
+            store_rows<D>(a, u, (wr * NBW + n) * 16 + r16, final, w.acc[n], w.m[n], l, quad);
+        }
+        return;
+    }
+
+    float* ml = lds;                                   // [WT][slots * 16][2]
+    float* xa = lds + (size_t)WT * slots * 16 * 2;     // [WT - 1][slots * 16][XP]
     __syncthreads();  // tile buffers are free from here on
 #pragma unroll
-    for (int n = 0; n < NBW; ++n) {
-        float* slot = mg + ((size_t)(tg * slots + wr * NBW + n) * 16 + r16) * MP;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) *(f32x4_t*)(slot + db * 16 + quad * 4) = w.acc[n][db];
+    for (int n = 0; n < NBW; ++n)
         if (quad == 0) {
-            slot[D] = w.m[n];
-            slot[D + 1] = w.l[n];
+            float* e = ml + ((size_t)(tg * slots + wr * NBW + n) * 16 + r16) * 2;
+            e[0] = w.m[n];
+            e[1] = w.l[n];
         }
-    }
     __syncthreads();
-    // Row r of token group t sits at mg[(t * slots * 16 + r) * MP].
-    const size_t tg_stride = (size_t)slots * 16 * MP;
-    for (int r = tid; r < R; r += nthreads) {
+    float rowM[NBW], rowL[NBW];
+#pragma unroll
+    for (int n = 0; n < NBW; ++n) {
+        const int srow = (wr * NBW + n) * 16 + r16;
         float M = kNegInf;
-        for (int t = 0; t < WT; ++t) M = fmaxf(M, mg[t * tg_stride + (size_t)r * MP + D]);
+        for (int t = 0; t < WT; ++t) M = fmaxf(M, ml[((size_t)t * slots * 16 + srow) * 2]);
         float L = 0.f;
         if (M != kNegInf)
-            for (int t = 0; t < WT; ++t)
-                L += fast_exp2(mg[t * tg_stride + (size_t)r * MP + D] - M) * mg[t * tg_stride + (size_t)r * MP + D + 1];
-        rowM[r] = M;
-        rowL[r] = L;
+            for (int t = 0; t < WT; ++t) {
+                const float* e = ml + ((size_t)t * slots * 16 + srow) * 2;
+                L += fast_exp2(e[0] - M) * e[1];
+            }
+        float alpha = w.m[n] == kNegInf ? 0.f : fast_exp2(w.m[n] - M);
+        if (final) alpha = L > 0.f ? alpha / L : 0.f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) w.acc[n][db] *= alpha;
+        rowM[n] = M;
+        rowL[n] = L;
+        if (tg > 0) {
+            float* x = xa + ((size_t)(tg - 1) * slots * 16 + srow) * XP;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) *(f32x4_t*)(x + db * 16 + quad * 4) = w.acc[n][db];
+        }
     }
     __syncthreads();
-    if (WT > 1) {
-        for (int idx = tid; idx < R * D; idx += nthreads) {
-            const int r = idx / D, d = idx - (idx / D) * D;
-            const float M = rowM[r];
-            float A = 0.f;
-            if (M != kNegInf)
-                for (int t = 0; t < WT; ++t)
-                    A += fast_exp2(mg[t * tg_stride + (size_t)r * MP + D] - M) * mg[t * tg_stride + (size_t)r * MP + d];
-            mg[(size_t)r * MP + d] = A;
+    if (tg != 0) return;
+#pragma unroll
+    for (int n = 0; n < NBW; ++n) {
+        if (!ALL_ON && !w.on[n]) continue;
+        const int srow = (wr * NBW + n) * 16 + r16;
+        for (int t = 1; t < WT; ++t) {
+            const float* x = xa + ((size_t)(t - 1) * slots * 16 + srow) * XP;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) w.acc[n][db] += *(const f32x4_t*)(x + db * 16 + quad * 4);
         }
-        __syncthreads();
-    }
-
-    if (u.S > 1) {
-        const size_t row0 = (size_t)blockIdx.x * R;
-        for (int idx = tid; idx < R * (D / 4); idx += nthreads) {
-            const int r = idx / (D / 4), d4 = idx - (idx / (D / 4)) * (D / 4);
-            *(f32x4_t*)(a.part_acc + (row0 + r) * D + 4 * d4) = *(const f32x4_t*)(mg + (size_t)r * MP + 4 * d4);
-        }
-        for (int r = tid; r < R; r += nthreads) {
-            a.part_m[row0 + r] = rowM[r];
-            a.part_l[row0 + r] = rowL[r];
-        }
-        return;  // the combine kernel finishes this (request, kv head)
-    }
-
-    // Final stage: out = acc / L, lse = M + log2 L.
-    for (int idx = tid; idx < R * D; idx += nthreads) {
-        const int r = idx / D, d = idx - (idx / D) * D;
-        const int i = r / a.g, h = u.hk * a.g + (r - (r / a.g) * a.g);
-        const float M = rowM[r], L = rowL[r];
-        const size_t orow = (size_t)(u.b * a.K + i) * a.Hq + h;
-        a.out[orow * D + d] = f32_to_bf16_rne(L > 0.f ? mg[(size_t)r * MP + d] / L : 0.f);
-        if (d == 0 && a.lse) a.lse[orow] = L > 0.f ? M + log2f(L) : kNegInf;
+        store_rows<D>(a, u, srow, final, w.acc[n], rowM[n], rowL[n], quad);
     }
 }
 
