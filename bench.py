@@ -220,6 +220,7 @@ def run_case(case, steps, warmup, threads, graph=True, splits=0, waves=0):
         "units": info["units"],
         "max_splits": info["max_splits"],
         "waves_per_unit": info["waves_per_unit"],
+        "shared_tiles": info["shared_tiles"],
         "combine_launch": info["combine_launch"],
     }
     plan.destroy()
@@ -277,14 +278,14 @@ def pmc_summary(case_name, fetch_path, write_path):
 
     Both counters are KiB per dispatch. Each is scaled by the factor that maps the
     reference copy's reading onto its known 1 GiB, then averaged over the
-    stream_kernel dispatches of the run."""
+    attention-kernel dispatches (stream_kernel or shared_kernel) of the run."""
     out = {"case": case_name, "kernel_digest": kernel_source_digest()}
     for tag, path, counter in (("fetch", fetch_path, "FETCH_SIZE"), ("write", write_path, "WRITE_SIZE")):
         rows = [r for r in _counter_rows(path) if r[1] == counter]
-        att = [v for k, _, v in rows if "stream_kernel" in k]
+        att = [v for k, _, v in rows if "stream_kernel" in k or "shared_kernel" in k]
         ref = [v for k, _, v in rows if "neg" in k.lower()]
         if not att or not ref:
-            raise SystemExit(f"{path}: {counter} rows for stream_kernel ({len(att)}) or the copy ({len(ref)}) missing")
+            raise SystemExit(f"{path}: {counter} rows for the attention kernel ({len(att)}) or the copy ({len(ref)}) missing")
         ref_kib = sum(ref) / len(ref)
         factor = (COPY_ELEMS * 4 / 1024) / ref_kib
         out[f"{tag}_kib_raw"] = round(sum(att) / len(att), 1)
@@ -426,7 +427,8 @@ def main():
                    "max_splits": res["max_splits"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "stream_kernel (split-KV paged attention)",
+                     "kernel": ("shared_kernel" if res["shared_tiles"] else "stream_kernel") +
+                               " (split-KV paged attention)",
                      "kernel_us": round(res["partial_ms"] * 1e3, 2), "kernel_events": res["kernel_timing"]},
         "cpu_baseline": None,
     }
