@@ -20,6 +20,8 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 PART_ALL, PART_CAUSAL, PART_FUTURE = 0, 1, 2
+KV_BF16, KV_FP8_E4M3 = 0, 1
+_KV_CODES = {"bf16": KV_BF16, "fp8_e4m3": KV_FP8_E4M3}
 
 
 class _Params(ctypes.Structure):
@@ -35,6 +37,9 @@ class _Params(ctypes.Structure):
         ("window_left", ctypes.c_int32),
         ("window_right", ctypes.c_int32),
         ("sm_scale", ctypes.c_double),
+        ("kv_dtype", ctypes.c_int32),
+        ("k_scale", ctypes.c_double),
+        ("v_scale", ctypes.c_double),
     ]
 
 
@@ -62,6 +67,8 @@ def _load():
     lib.oracle_merge.restype = None
     lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_to_double.restype = ctypes.c_double
+    lib.oracle_fp8_e4m3_to_double.argtypes = [ctypes.c_uint8]
+    lib.oracle_fp8_e4m3_to_double.restype = ctypes.c_double
     _lib = lib
     return lib
 
@@ -74,21 +81,27 @@ def default_threads() -> int:
 
 
 def attention(q, k_pool, v_pool, page_table, seq_lens, *, block_size, num_q_heads, num_kv_heads, head_dim,
-              page_size, sm_scale, window_left=-1, window_right=-1, part=PART_ALL, pairs=None, threads=None):
+              page_size, sm_scale, window_left=-1, window_right=-1, part=PART_ALL, pairs=None, threads=None,
+              kv_dtype="bf16", k_scale=1.0, v_scale=1.0):
     """Return (out [B,K,Hq,D] float64, lse2 [B,K,Hq] float64) straight from the definition.
 
-    ``q``, ``k_pool`` and ``v_pool`` hold bf16 bit patterns (uint16). ``pairs``
-    optionally restricts the work to a list of (b, h_kv); other rows are NaN.
+    ``q`` holds bf16 bit patterns (uint16); ``k_pool`` and ``v_pool`` hold bf16
+    bits (uint16) or OCP fp8 e4m3 bytes (uint8, ``kv_dtype="fp8_e4m3"``) that
+    stand for ``k_scale`` / ``v_scale`` times their value. ``pairs`` optionally
+    restricts the work to a list of (b, h_kv); other rows are NaN.
     """
     lib = _load()
+    code = _KV_CODES[kv_dtype]
+    el = np.uint8 if code == KV_FP8_E4M3 else np.uint16
     q = np.ascontiguousarray(q, dtype=np.uint16)
-    k_pool = np.ascontiguousarray(k_pool, dtype=np.uint16)
-    v_pool = np.ascontiguousarray(v_pool, dtype=np.uint16)
+    k_pool = np.ascontiguousarray(k_pool, dtype=el)
+    v_pool = np.ascontiguousarray(v_pool, dtype=el)
     page_table = np.ascontiguousarray(page_table, dtype=np.int32)
     seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
     B = int(seq_lens.shape[0])
     prm = _Params(B, block_size, num_q_heads, num_kv_heads, head_dim, page_size, int(page_table.shape[1]),
-                  int(k_pool.shape[0]), window_left, window_right, float(sm_scale))
+                  int(k_pool.shape[0]), window_left, window_right, float(sm_scale), code, float(k_scale),
+                  float(v_scale))
     out = np.full((B, block_size, num_q_heads, head_dim), np.nan)
     lse2 = np.full((B, block_size, num_q_heads), np.nan)
     if pairs is not None:
@@ -112,7 +125,8 @@ def attention_case(inputs, *, part=PART_ALL, pairs=None, threads=None, window_le
                      head_dim=c.head_dim, page_size=c.page_size, sm_scale=c.scale,
                      window_left=c.window_left if window_left is None else window_left,
                      window_right=c.window_right if window_right is None else window_right,
-                     part=part, pairs=pairs, threads=threads)
+                     part=part, pairs=pairs, threads=threads, kv_dtype=c.kv_dtype, k_scale=c.k_scale,
+                     v_scale=c.v_scale)
 
 
 def merge(out_a, lse_a, out_b, lse_b):
@@ -133,3 +147,7 @@ def merge(out_a, lse_a, out_b, lse_b):
 
 def bf16_to_double(bits: int) -> float:
     return float(_load().oracle_bf16_to_double(bits))
+
+
+def fp8_e4m3_to_double(code: int) -> float:
+    return float(_load().oracle_fp8_e4m3_to_double(code))

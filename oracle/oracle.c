@@ -35,6 +35,13 @@
  *  - Paged reads (PR #20374 sweep setup: page 32, "HND" layout): key j of
  *    request b is slot j mod P of page page_table[b, j / P]; a pool is
  *    [pages, Hkv, P, D]. Query head h reads kv head h / (Hq / Hkv).
+ *
+ *  - fp8 context storage (TensorRT-LLM PR #16150, paged DFlash context read from
+ *    the target KV cache manager's pool: the kernel supports fp8 context storage,
+ *    with bf16 dots and fp32 accumulation). The pages fix no format; read here as
+ *    OCP E4M3 bytes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ *    exponent field 0 encodes subnormals m * 2^-9; S.1111.111 is NaN, there is no
+ *    infinity), each standing for scale * value, one scale per pool.
  */
 #include "oracle.h"
 
@@ -50,10 +57,24 @@ double oracle_bf16_to_double(uint16_t bits) {
     return (double)f;
 }
 
+double oracle_fp8_e4m3_to_double(uint8_t code) {
+    const int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+    return sign ? -v : v;
+}
+
+/* Element d of a K or V row, decoded and scaled. */
+static double kv_elem(const oracle_params* prm, const void* pool, int64_t row_elem, int d, double scale) {
+    if (prm->kv_dtype == ORACLE_KV_FP8_E4M3) return scale * oracle_fp8_e4m3_to_double(((const uint8_t*)pool)[row_elem + d]);
+    return scale * oracle_bf16_to_double(((const uint16_t*)pool)[row_elem + d]);
+}
+
 typedef struct {
     const oracle_params* prm;
     int part;
-    const uint16_t *q, *k, *v;
+    const uint16_t* q;
+    const void *k, *v;
     const int32_t *pt, *lens;
     const int32_t* rows; /* triples (b, i, h) */
     int64_t n_rows;
@@ -63,11 +84,11 @@ typedef struct {
     int64_t max_keys;
 } oracle_job;
 
-static const uint16_t* key_row(const oracle_params* prm, const uint16_t* pool, const int32_t* pt, int b, int hk,
-                               int64_t j) {
+/* Element index of the first element of key j's row (kv head hk) in a pool. */
+static int64_t key_row(const oracle_params* prm, const int32_t* pt, int b, int hk, int64_t j) {
     const int64_t page = pt[(int64_t)b * prm->page_table_stride + j / prm->page_size];
     const int64_t slot = j % prm->page_size;
-    return pool + ((page * prm->num_kv_heads + hk) * prm->page_size + slot) * prm->head_dim;
+    return ((page * prm->num_kv_heads + hk) * prm->page_size + slot) * prm->head_dim;
 }
 
 static void one_row(oracle_job* job, int b, int i, int h, double* s) {
@@ -99,9 +120,9 @@ static void one_row(oracle_job* job, int b, int i, int h, double* s) {
 
     double m = -INFINITY;
     for (int64_t j = lo; j <= hi; ++j) {
-        const uint16_t* kr = key_row(prm, job->k, job->pt, b, hk, j);
+        const int64_t kr = key_row(prm, job->pt, b, hk, j);
         double dot = 0.0;
-        for (int d = 0; d < D; ++d) dot += qd[d] * oracle_bf16_to_double(kr[d]);
+        for (int d = 0; d < D; ++d) dot += qd[d] * kv_elem(prm, job->k, kr, d, prm->k_scale);
         s[j - lo] = prm->sm_scale * dot;
         if (s[j - lo] > m) m = s[j - lo];
     }
@@ -111,8 +132,8 @@ static void one_row(oracle_job* job, int b, int i, int h, double* s) {
     for (int64_t j = lo; j <= hi; ++j) {
         const double e = exp(s[j - lo] - m);
         z += e;
-        const uint16_t* vr = key_row(prm, job->v, job->pt, b, hk, j);
-        for (int d = 0; d < D; ++d) acc[d] += e * oracle_bf16_to_double(vr[d]);
+        const int64_t vr = key_row(prm, job->pt, b, hk, j);
+        for (int d = 0; d < D; ++d) acc[d] += e * kv_elem(prm, job->v, vr, d, prm->v_scale);
     }
     for (int d = 0; d < D; ++d) o[d] = acc[d] / z;
     job->lse2[row] = (m + log(z)) / log(2.0);
@@ -133,8 +154,8 @@ static void* worker(void* arg) {
     return NULL;
 }
 
-int oracle_attention(const oracle_params* prm, int part, const uint16_t* q, const uint16_t* k_pool,
-                     const uint16_t* v_pool, const int32_t* page_table, const int32_t* seq_lens,
+int oracle_attention(const oracle_params* prm, int part, const uint16_t* q, const void* k_pool,
+                     const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
                      const int32_t* pairs, int n_pairs, double* out, double* lse2, int threads) {
     if (!prm || !q || !k_pool || !v_pool || !page_table || !seq_lens || !out || !lse2) return -1;
     if (prm->batch < 1 || prm->block_size < 1 || prm->num_kv_heads < 1 || prm->num_q_heads < 1 ||
@@ -142,6 +163,8 @@ int oracle_attention(const oracle_params* prm, int part, const uint16_t* q, cons
         prm->page_size < 1 || prm->page_table_stride < 1 || prm->num_pages < 1)
         return -1;
     if (part < ORACLE_PART_ALL || part > ORACLE_PART_FUTURE) return -1;
+    if (prm->kv_dtype != ORACLE_KV_BF16 && prm->kv_dtype != ORACLE_KV_FP8_E4M3) return -1;
+    if (!isfinite(prm->k_scale) || !isfinite(prm->v_scale)) return -1;
     if (prm->window_left == 0 || prm->window_left < -1 || prm->window_right < -1) return -1;
 
     int64_t max_keys = 0;

@@ -26,13 +26,19 @@ typedef struct oracle_params {
     int32_t window_left;       /* -1: no left limit; W >= 1: keys (p - W, p] on the causal side */
     int32_t window_right;      /* -1: every later block key; 0: none; > 0: at most that many */
     double sm_scale;
+    int32_t kv_dtype;          /* ORACLE_KV_BF16 or ORACLE_KV_FP8_E4M3: element type of both pools */
+    double k_scale;            /* a stored key element stands for k_scale times its decoded value */
+    double v_scale;            /* likewise for values */
 } oracle_params;
+
+enum { ORACLE_KV_BF16 = 0, ORACLE_KV_FP8_E4M3 = 1 };
 
 enum { ORACLE_PART_ALL = 0, ORACLE_PART_CAUSAL = 1, ORACLE_PART_FUTURE = 2 };
 
 /*
  * Attention of every query row over its key set, straight from the definition.
- * q: bf16 bits [B, K, Hq, D]; k_pool, v_pool: bf16 bits [pages, Hkv, P, D];
+ * q: bf16 bits [B, K, Hq, D]; k_pool, v_pool: [pages, Hkv, P, D] elements of
+ * kv_dtype (bf16 bits or OCP fp8 e4m3 bytes), scaled by k_scale / v_scale;
  * page_table: int32 [B, stride]; seq_lens: int32 [B] (context + K keys).
  * pairs: optional list of n_pairs (b, h_kv) int32 pairs; when NULL every pair
  * is computed. out: double [B, K, Hq, D]; lse2: double [B, K, Hq] (base-2
@@ -40,8 +46,8 @@ enum { ORACLE_PART_ALL = 0, ORACLE_PART_CAUSAL = 1, ORACLE_PART_FUTURE = 2 };
  * untouched. An empty key set gives out = 0, lse2 = -inf.
  * Returns 0, or -1 on invalid arguments.
  */
-int oracle_attention(const oracle_params* prm, int part, const uint16_t* q, const uint16_t* k_pool,
-                     const uint16_t* v_pool, const int32_t* page_table, const int32_t* seq_lens,
+int oracle_attention(const oracle_params* prm, int part, const uint16_t* q, const void* k_pool,
+                     const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
                      const int32_t* pairs, int n_pairs, double* out, double* lse2, int threads);
 
 /* Log-sum-exp merge of two normalised attention results over disjoint key sets. */
@@ -50,6 +56,9 @@ void oracle_merge(int64_t rows, int32_t head_dim, const double* out_a, const dou
 
 /* Exact bf16 -> double widening used by the oracle (exported for its tests). */
 double oracle_bf16_to_double(uint16_t bits);
+
+/* Exact OCP fp8 e4m3 -> double decoding used by the oracle (exported for its tests). */
+double oracle_fp8_e4m3_to_double(uint8_t code);
 
 #ifdef __cplusplus
 }

@@ -20,6 +20,7 @@ _LIB_PATH = os.path.join(_HERE, "libsynth.so")
 _lib = None
 
 BF16_NAN = 0x7FC0
+FP8_NAN = 0x7F  # OCP E4M3 NaN
 
 
 def build() -> str:
@@ -56,7 +57,10 @@ def _load():
     lib.synth_pages_needed.restype = i64
     lib.synth_page_table.argtypes = [u64, i32, ptr, i32, i32, ptr]
     lib.synth_page_table.restype = i32
-    lib.synth_fill_kv.argtypes = [u64, i32, i32, ptr, i32, i32, i32, i32, ptr, i64, dbl, dbl, ctypes.c_uint16, ptr, i32]
+    lib.synth_fill_kv.argtypes = [u64, i32, i32, ptr, i32, i32, i32, i32, ptr, i64, dbl, dbl, i32, dbl, ctypes.c_uint16,
+                                  ptr, i32]
+    lib.synth_e4m3_from_double.argtypes = [dbl]
+    lib.synth_e4m3_from_double.restype = ctypes.c_uint8
     lib.synth_fill_kv.restype = i32
     _lib = lib
     return lib
@@ -79,8 +83,8 @@ class Inputs:
     """One case's inputs, all host numpy arrays.
 
     q            uint16 (bf16 bits) [B, K, Hq, D]
-    k_pool       uint16 [num_pages, Hkv, P, D]
-    v_pool       uint16 [num_pages, Hkv, P, D]
+    k_pool       [num_pages, Hkv, P, D]: uint16 bf16 bits, or uint8 fp8 E4M3 bytes
+    v_pool       same as k_pool (case.kv_dtype; elements stand for scale * value)
     page_table   int32 [B, stride]
     seq_lens     int32 [B]   keys in cache per request, block included (C_b + K)
     """
@@ -129,19 +133,23 @@ def make_q(case: Case, threads: int | None = None) -> np.ndarray:
 
 
 def make_pool(case: Case, tensor_id: int, seq_lens: np.ndarray, page_table: np.ndarray, num_pages: int,
-              fill: int = BF16_NAN, threads: int | None = None) -> np.ndarray:
+              fill: int | None = None, threads: int | None = None) -> np.ndarray:
     lib = _load()
-    pool = np.empty((num_pages, case.num_kv_heads, case.page_size, case.head_dim), dtype=np.uint16)
+    fp8 = case.kv_dtype == "fp8_e4m3"
+    if fill is None:
+        fill = FP8_NAN if fp8 else BF16_NAN
+    scale = case.k_scale if tensor_id == 2 else case.v_scale
+    pool = np.empty((num_pages, case.num_kv_heads, case.page_size, case.head_dim), dtype=np.uint8 if fp8 else np.uint16)
     rc = lib.synth_fill_kv(case.seed, tensor_id, case.batch, _p(seq_lens), case.num_kv_heads, case.head_dim,
                            case.page_size, page_table.shape[1], _p(page_table), num_pages,
-                           float(case.outlier_rate), float(case.outlier_scale), fill, _p(pool),
-                           threads or default_threads())
+                           float(case.outlier_rate), float(case.outlier_scale), 1 if fp8 else 0, 1.0 / float(scale),
+                           fill, _p(pool), threads or default_threads())
     if rc != 0:
         raise ValueError(f"synth_fill_kv failed ({rc})")
     return pool
 
 
-def make_inputs(case: Case, fill: int = BF16_NAN, threads: int | None = None) -> Inputs:
+def make_inputs(case: Case, fill: int | None = None, threads: int | None = None) -> Inputs:
     """Generate every input of a case (pools include one fill page; see synth.c)."""
     lib = _load()
     seq_lens = seq_lens_for(case)
@@ -151,6 +159,11 @@ def make_inputs(case: Case, fill: int = BF16_NAN, threads: int | None = None) ->
     k_pool = make_pool(case, 2, seq_lens, pt, num_pages, fill, threads)
     v_pool = make_pool(case, 3, seq_lens, pt, num_pages, fill, threads)
     return Inputs(case, q, k_pool, v_pool, pt, seq_lens)
+
+
+def e4m3_from_double(x: float) -> int:
+    """OCP fp8 E4M3 encoding (round to nearest even, saturating at +-448) of one value."""
+    return int(_load().synth_e4m3_from_double(float(x)))
 
 
 def bf16_bits_to_float(bits: np.ndarray) -> np.ndarray:

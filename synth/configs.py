@@ -12,7 +12,7 @@ holds context + K keys.
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 
 
 @dataclass(frozen=True)
@@ -33,6 +33,9 @@ class Case:
     outlier_rate: float = 0.0
     outlier_scale: float = 8.0
     sm_scale: float = field(default=0.0)
+    kv_dtype: str = "bf16"                  # "bf16" or "fp8_e4m3": element type of the K and V pools
+    k_scale: float = 1.0                    # a stored key element stands for k_scale times its value
+    v_scale: float = 1.0
 
     @property
     def seed(self) -> int:
@@ -107,7 +110,22 @@ def all_cases() -> list:
 
 
 def find_case(name: str) -> Case:
+    """A configuration case by name; a "_fp8" suffix selects its fp8 E4M3 variant."""
+    if name.endswith("_fp8"):
+        return fp8_variant(find_case(name[: -len("_fp8")]))
     for c in all_cases():
         if c.name == name:
             return c
     raise KeyError(name)
+
+
+# fp8 context storage: the same case with both pools held as OCP fp8 E4M3 bytes.
+# The N(0,1) draws are divided by the pool scale before encoding; 1/16 maps them
+# (|x| < 6) below 96, inside the format's range (448), and off its subnormals for
+# |x| > 2^-10. Outlier keys scaled x8 may saturate at 448.
+FP8_SCALE = 0.0625
+
+
+def fp8_variant(case: Case, k_scale: float = FP8_SCALE, v_scale: float = FP8_SCALE) -> Case:
+    """A copy of `case` whose K and V pools are fp8 E4M3 with the given per-pool scales."""
+    return replace(case, name=case.name + "_fp8", kv_dtype="fp8_e4m3", k_scale=k_scale, v_scale=v_scale)

@@ -75,6 +75,30 @@ uint16_t synth_bf16_from_double(double x) {
     return (uint16_t)(u >> 16);
 }
 
+/* OCP fp8 E4M3 (bias 7, 3 mantissa bits, no infinity, S.1111.111 = NaN) by
+ * round-to-nearest-even, saturating at +-448. Input data preparation only. */
+uint8_t synth_e4m3_from_double(double x) {
+    if (isnan(x)) return 0x7F;
+    const uint8_t s = signbit(x) ? 0x80 : 0x00;
+    double a = fabs(x);
+    if (a >= 448.0) return s | 0x7E;
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal range: multiples of 2^-9; 8 * 2^-9 is the smallest normal (code 0x08) */
+        const double q = nearbyint(ldexp(a, 9));
+        return s | (uint8_t)q;
+    }
+    int e;
+    frexp(a, &e); /* a = f * 2^e, f in [0.5, 1): the leading bit is 2^(e-1) */
+    e -= 1;
+    double q = nearbyint(ldexp(a, 3 - e)); /* 8..16 steps of 2^(e-3) */
+    if (q >= 16.0) {
+        q = 8.0;
+        e += 1;
+    }
+    if (e > 8 || (e == 8 && q > 14.0)) return s | 0x7E;
+    return s | (uint8_t)(((e + 7) << 3) | ((int)q - 8));
+}
+
 /* ---------------- q ---------------- */
 
 typedef struct {
@@ -158,26 +182,33 @@ int synth_page_table(uint64_t seed, int batch, const int32_t* seq_lens, int page
 
 typedef struct {
     uint64_t key, outlier_key;
-    double outlier_rate, outlier_scale;
-    int batch, num_kv_heads, head_dim, page_size, stride;
+    double outlier_rate, outlier_scale, inv_scale;
+    int batch, num_kv_heads, head_dim, page_size, stride, fp8;
     const int32_t* seq_lens;
     const int32_t* page_table;
     uint16_t fill;
-    uint16_t* pool;
+    void* pool;
     int64_t num_pages;
     int32_t* owner_b;  /* per page: request, or -1 for unused pages */
     int32_t* owner_lp; /* per page: logical page index within the request */
     int64_t lo, hi;    /* page range of this worker */
 } kv_job;
 
+static void put(const kv_job* j, size_t idx, uint16_t bits) {
+    if (j->fp8)
+        ((uint8_t*)j->pool)[idx] = (uint8_t)bits;
+    else
+        ((uint16_t*)j->pool)[idx] = bits;
+}
+
 static void* kv_worker(void* arg) {
     kv_job* j = (kv_job*)arg;
     const int P = j->page_size, D = j->head_dim, H = j->num_kv_heads;
     for (int64_t pid = j->lo; pid < j->hi; ++pid) {
-        uint16_t* page = j->pool + (size_t)pid * (size_t)H * P * D;
+        const size_t page = (size_t)pid * (size_t)H * P * D;
         const int b = j->owner_b[pid];
         if (b < 0) {
-            for (size_t e = 0; e < (size_t)H * P * D; ++e) page[e] = j->fill;
+            for (size_t e = 0; e < (size_t)H * P * D; ++e) put(j, page + e, j->fill);
             continue;
         }
         const int64_t n_b = j->seq_lens[b];
@@ -187,16 +218,17 @@ static void* kv_worker(void* arg) {
             if (tok < n_b && j->outlier_rate > 0.0)
                 outlier = synth_uniform(j->outlier_key, (uint64_t)b * SYNTH_TOKEN_SPAN + (uint64_t)tok) < j->outlier_rate;
             for (int h = 0; h < H; ++h) {
-                uint16_t* row = page + ((size_t)h * P + slot) * D;
+                const size_t row = page + ((size_t)h * P + slot) * D;
                 if (tok >= n_b) {
-                    for (int d = 0; d < D; ++d) row[d] = j->fill;
+                    for (int d = 0; d < D; ++d) put(j, row + d, j->fill);
                     continue;
                 }
                 const uint64_t base = (((uint64_t)b * SYNTH_TOKEN_SPAN + (uint64_t)tok) * (uint64_t)H + (uint64_t)h) * (uint64_t)D;
                 for (int d = 0; d < D; ++d) {
                     double x = synth_normal(j->key, base + (uint64_t)d);
                     if (outlier) x *= j->outlier_scale;
-                    row[d] = synth_bf16_from_double(x);
+                    x *= j->inv_scale;
+                    put(j, row + d, j->fp8 ? synth_e4m3_from_double(x) : synth_bf16_from_double(x));
                 }
             }
         }
@@ -206,7 +238,7 @@ static void* kv_worker(void* arg) {
 
 int synth_fill_kv(uint64_t seed, int tensor_id, int batch, const int32_t* seq_lens, int num_kv_heads, int head_dim,
                   int page_size, int stride, const int32_t* page_table, int64_t num_pages, double outlier_rate,
-                  double outlier_scale, uint16_t fill, uint16_t* pool, int threads) {
+                  double outlier_scale, int fp8, double inv_scale, uint16_t fill, void* pool, int threads) {
     threads = clamp_threads(threads);
     int32_t* owner_b = (int32_t*)malloc(sizeof(int32_t) * (size_t)num_pages);
     int32_t* owner_lp = (int32_t*)malloc(sizeof(int32_t) * (size_t)num_pages);
@@ -237,6 +269,8 @@ int synth_fill_kv(uint64_t seed, int tensor_id, int batch, const int32_t* seq_le
         j->outlier_key = synth_key(seed, SYNTH_TENSOR_OUTLIER);
         j->outlier_rate = tensor_id == SYNTH_TENSOR_K ? outlier_rate : 0.0;
         j->outlier_scale = outlier_scale;
+        j->inv_scale = inv_scale;
+        j->fp8 = fp8;
         j->batch = batch;
         j->num_kv_heads = num_kv_heads;
         j->head_dim = head_dim;

@@ -36,11 +36,17 @@ int64_t synth_pages_needed(int batch, const int32_t* seq_lens, int page_size);
 int synth_page_table(uint64_t seed, int batch, const int32_t* seq_lens, int page_size, int stride,
                      int32_t* page_table);
 
-/* Fill a [num_pages, Hkv, P, D] bf16 pool. For tensor_id == K, each (b, token) is an
- * outlier with probability outlier_rate and its keys are multiplied by outlier_scale. */
+/* Fill a [num_pages, Hkv, P, D] pool with element j of token t, kv head h drawn
+ * N(0,1), divided by the pool's scale (inv_scale = 1 / scale) and stored as bf16
+ * (fp8 = 0) or OCP fp8 E4M3 bytes (fp8 = 1). For tensor_id == K, each
+ * (b, token) is an outlier with probability outlier_rate and its keys are
+ * multiplied by outlier_scale. Unused slots get `fill` (its low byte for fp8). */
 int synth_fill_kv(uint64_t seed, int tensor_id, int batch, const int32_t* seq_lens, int num_kv_heads, int head_dim,
                   int page_size, int stride, const int32_t* page_table, int64_t num_pages, double outlier_rate,
-                  double outlier_scale, uint16_t fill, uint16_t* pool, int threads);
+                  double outlier_scale, int fp8, double inv_scale, uint16_t fill, void* pool, int threads);
+
+/* OCP fp8 E4M3 encoding by round-to-nearest-even, saturating at +-448. */
+uint8_t synth_e4m3_from_double(double x);
 
 #ifdef __cplusplus
 }

@@ -10,16 +10,25 @@ from __future__ import annotations
 import math
 
 import numpy as np
+import torch
 from scipy.special import logsumexp, softmax
 
 from synth import bf16_bits_to_float
 
 
-def dense_kv(pool: np.ndarray, page_table: np.ndarray, b: int, n: int) -> np.ndarray:
-    """[n, Hkv, D] float64 view of request b's keys (or values) in logical order."""
+def decode_pool(raw: np.ndarray) -> np.ndarray:
+    """Element values of pool pages: bf16 bits (uint16) by bit widening, OCP fp8 E4M3 bytes
+    (uint8) through torch's float8_e4m3fn conversion (a library decoder, not the oracle's)."""
+    if raw.dtype == np.uint8:
+        return torch.from_numpy(np.ascontiguousarray(raw)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return bf16_bits_to_float(raw).astype(np.float64)
+
+
+def dense_kv(pool: np.ndarray, page_table: np.ndarray, b: int, n: int, scale: float = 1.0) -> np.ndarray:
+    """[n, Hkv, D] float64 view of request b's keys (or values) in logical order, times the pool scale."""
     P = pool.shape[2]
     pages = page_table[b, : (n + P - 1) // P]
-    blk = bf16_bits_to_float(pool[pages]).astype(np.float64)  # [np, Hkv, P, D]
+    blk = scale * decode_pool(pool[pages])  # [np, Hkv, P, D]
     blk = np.transpose(blk, (0, 2, 1, 3)).reshape(-1, pool.shape[1], pool.shape[3])
     return blk[:n]
 
@@ -55,8 +64,8 @@ def attention(inputs, window_left=None, window_right=None, part="all"):
     q = bf16_bits_to_float(inputs.q).astype(np.float64)
     for b in range(B):
         n = int(inputs.seq_lens[b])
-        kd = dense_kv(inputs.k_pool, inputs.page_table, b, n)
-        vd = dense_kv(inputs.v_pool, inputs.page_table, b, n)
+        kd = dense_kv(inputs.k_pool, inputs.page_table, b, n, c.k_scale)
+        vd = dense_kv(inputs.v_pool, inputs.page_table, b, n, c.v_scale)
         mask = key_mask(n, K, g, wl, wr, part)
         for hk in range(Hkv):
             qr = q[b, :, hk * g:(hk + 1) * g, :].reshape(K * g, D)
