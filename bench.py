@@ -48,12 +48,13 @@ def log(msg):
 
 
 def kv_bytes(case, seq_lens) -> int:
-    """Algorithmic KV bytes of one call: every key a row needs, read once (K and V, 2 B each)."""
+    """Algorithmic KV bytes of one call: every key a row needs, read once (K and V, 2 B each for bf16, 1 for fp8)."""
+    eb = 1 if case.kv_dtype == "fp8_e4m3" else 2
     total = 0
     for n in seq_lens.tolist():
         c = n - case.block_size
         lo = max(0, c - case.window_left + 1) if case.window_left > 0 else 0
-        total += case.num_kv_heads * (n - lo) * 4 * case.head_dim
+        total += case.num_kv_heads * (n - lo) * 2 * eb * case.head_dim
     return total
 
 
@@ -96,7 +97,7 @@ class HipEvents:
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for name in ("kernels.hip", "api.cpp", "internal.h"):
+    for name in ("attention_kernels.h", "kernels_bf16.hip", "kernels_fp8.hip", "api.cpp", "internal.h"):
         with open(os.path.join(ROOT, "speculative_decoding_draft_paged_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -131,7 +132,8 @@ def run_case(case, steps, warmup, threads, graph=True, splits=0, waves=0):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
 
     q = bf(inp.q)
-    k0, v0 = bf(inp.k_pool), bf(inp.v_pool)
+    kv = (lambda a: torch.from_numpy(a).to(dev)) if inp.k_pool.dtype == np.uint8 else bf
+    k0, v0 = kv(inp.k_pool), kv(inp.v_pool)
     pt = torch.from_numpy(inp.page_table).to(dev)
     lens = torch.from_numpy(inp.seq_lens).to(dev)
     pool_bytes = 2 * inp.k_pool.nbytes
@@ -144,7 +146,7 @@ def run_case(case, steps, warmup, threads, graph=True, splits=0, waves=0):
                          num_kv_heads=case.num_kv_heads, head_dim=case.head_dim, page_size=case.page_size,
                          page_table_stride=inp.page_table.shape[1], num_pages=inp.num_pages, sm_scale=case.scale,
                          window_left=case.window_left, window_right=case.window_right, splits_override=splits,
-                         waves_override=waves)
+                         waves_override=waves, kv_dtype=case.kv_dtype, k_scale=case.k_scale, v_scale=case.v_scale)
     nbytes = ba.blockattn_workspace_size(prm, inp.seq_lens)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     plan = ba.blockattn_plan(prm, inp.seq_lens, ws, nbytes)
@@ -371,7 +373,7 @@ def main():
 
     import torch
 
-    from synth.configs import cases_for_config, find_case
+    from synth.configs import cases_for_config, find_case, fp8_variant
 
     threads = min(16, len(os.sched_getaffinity(0)))
 
@@ -389,6 +391,8 @@ def main():
     if args.sweep:
         sweep = []
         for c in cases_for_config(case.cfg):
+            if case.kv_dtype != "bf16":
+                c = fp8_variant(c, case.k_scale, case.v_scale)
             r, _, _ = run_case(c, max(10, args.steps // 2), 3, threads, graph=not args.eager, splits=args.splits,
                                waves=args.waves)
             r["gbs"] = r["kv_bytes"] / (r["step_ms"] * 1e-3) / 1e9
@@ -422,7 +426,8 @@ def main():
         "config": {"workload": f"{case.name}: draft-block attention, {case.num_q_heads}q/{case.num_kv_heads}kv heads, "
                                f"head_dim {case.head_dim}, K={case.block_size}, page {case.page_size}, "
                                f"{'windowed W=%d' % case.window_left if case.windowed else 'unwindowed'}",
-                   "batch": case.batch, "context": case.context, "kv_bytes_per_call": kvb,
+                   "batch": case.batch, "context": case.context, "kv_dtype": case.kv_dtype,
+                   "k_scale": case.k_scale, "v_scale": case.v_scale, "kv_bytes_per_call": kvb,
                    "pool_copies_rotated": res["copies"], "hip_graph": res["graph"], "units": res["units"],
                    "max_splits": res["max_splits"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

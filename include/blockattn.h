@@ -28,9 +28,10 @@
  *
  * Layouts (all contiguous, row-major, device memory unless stated):
  *   q, out      bf16 [B, K, Hq, D]
- *   k_cache,    bf16 [num_pages, Hkv, P, D] each ("HND" pages, PR #20374 sweep
- *   v_cache          setup); key j of request b is slot j % P of page
- *                    page_table[b, j / P]
+ *   k_cache,    [num_pages, Hkv, P, D] each ("HND" pages, PR #20374 sweep
+ *   v_cache          setup) of bf16, or of fp8 E4M3 bytes (kv_dtype); key j of
+ *                    request b is slot j % P of page page_table[b, j / P]; a
+ *                    stored key stands for k_scale * k, a value for v_scale * v
  *   page_table  int32 [B, page_table_stride]; entries past ceil(N_b / P) are
  *               never read
  *   seq_lens    int32 [B] = C_b + K, context plus the appended block
@@ -81,9 +82,18 @@ typedef struct blockattn_params {
     int32_t splits_override;   /* 0: automatic split count. > 0: exactly that many KV splits per
                                   (request, kv head), clamped to the request's 32-token tile count
                                   (for testing split invariance and tuning) */
-    int32_t waves_override;    /* 0: automatic. > 0: tile-streaming wavefronts per workgroup (1..8),
-                                  reduced if the row-waves of a tile leave no room (tuning) */
+    int32_t waves_override;    /* 0: automatic. > 0: wavefronts per workgroup (1..8): token groups when
+                                  R <= 32, row-waves (one or two row blocks each) when R > 32 (tuning) */
+    int32_t kv_dtype;          /* element type of k_cache and v_cache: BLOCKATTN_KV_BF16, or
+                                  BLOCKATTN_KV_FP8_E4M3 (OCP fp8 E4M3 bytes: 1 sign, 4 exponent bits
+                                  with bias 7, 3 mantissa bits, S.1111.111 = NaN; TensorRT-LLM PR #16150,
+                                  the paged DFlash context kernel supports fp8 context storage) */
+    float k_scale;             /* finite and > 0: a stored key element stands for k_scale times its
+                                  value (1 for an unscaled cache) */
+    float v_scale;             /* finite: a stored value element stands for v_scale times its value */
 } blockattn_params;
+
+enum { BLOCKATTN_KV_BF16 = 0, BLOCKATTN_KV_FP8_E4M3 = 1 };
 
 typedef struct blockattn_plan_s* blockattn_plan_t;
 
@@ -130,7 +140,7 @@ int blockattn_plan(const blockattn_params* params, const int32_t* seq_lens_host,
 
 /*
  * Non-causal unwindowed block attention (the plan must have window_left = -1).
- * q, k_cache, v_cache: bf16 device buffers (layouts above); page_table,
+ * q: bf16, k_cache and v_cache: kv_dtype device buffers (layouts above); page_table,
  * seq_lens: int32 device buffers; workspace: the buffer given to the plan;
  * out: bf16 [B, K, Hq, D]; lse: fp32 [B, K, Hq] or NULL; stream: hipStream_t.
  * Launch only: no allocation, no host synchronisation.

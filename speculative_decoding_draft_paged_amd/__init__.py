@@ -26,6 +26,8 @@ BLOCKATTN_ERR_UNSUPPORTED = 2
 BLOCKATTN_ERR_WORKSPACE_TOO_SMALL = 3
 BLOCKATTN_ERR_PLAN_MISMATCH = 4
 BLOCKATTN_ERR_HIP = 5
+BLOCKATTN_KV_BF16 = 0
+BLOCKATTN_KV_FP8_E4M3 = 1
 
 EXPORTED = (
     "blockattn_workspace_size",
@@ -54,6 +56,9 @@ class blockattn_params(ctypes.Structure):
         ("sm_scale", ctypes.c_float),
         ("splits_override", ctypes.c_int32),
         ("waves_override", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
@@ -124,10 +129,16 @@ def _check(status: int):
         raise BlockAttnError(status, blockattn_last_error())
 
 
+KV_DTYPES = {"bf16": BLOCKATTN_KV_BF16, "fp8_e4m3": BLOCKATTN_KV_FP8_E4M3}
+
+
 def make_params(*, batch, block_size, num_q_heads, num_kv_heads, head_dim, page_size, page_table_stride, num_pages,
-                sm_scale, window_left=-1, window_right=-1, splits_override=0, waves_override=0) -> blockattn_params:
+                sm_scale, window_left=-1, window_right=-1, splits_override=0, waves_override=0, kv_dtype="bf16",
+                k_scale=1.0, v_scale=1.0) -> blockattn_params:
+    code = KV_DTYPES[kv_dtype] if isinstance(kv_dtype, str) else int(kv_dtype)
     return blockattn_params(batch, block_size, num_q_heads, num_kv_heads, head_dim, page_size, page_table_stride,
-                            num_pages, window_left, window_right, float(sm_scale), splits_override, waves_override)
+                            num_pages, window_left, window_right, float(sm_scale), splits_override, waves_override,
+                            code, float(k_scale), float(v_scale))
 
 
 def _host_lens(seq_lens_host):
@@ -243,8 +254,9 @@ def _check_buffers(plan: Plan, q, k_cache, v_cache, page_table, seq_lens, out, l
     _expect("q", q, rows * p.head_dim, ("bfloat16", "int16", "uint16"))
     _expect("out", out, rows * p.head_dim, ("bfloat16", "int16", "uint16"))
     pool = p.num_pages * p.num_kv_heads * p.page_size * p.head_dim
-    _expect("k_cache", k_cache, pool, ("bfloat16", "int16", "uint16"))
-    _expect("v_cache", v_cache, pool, ("bfloat16", "int16", "uint16"))
+    kv = ("uint8", "int8", "float8_e4m3fn") if p.kv_dtype == BLOCKATTN_KV_FP8_E4M3 else ("bfloat16", "int16", "uint16")
+    _expect("k_cache", k_cache, pool, kv)
+    _expect("v_cache", v_cache, pool, kv)
     _expect("page_table", page_table, p.batch * p.page_table_stride, ("int32",))
     _expect("seq_lens", seq_lens, p.batch, ("int32",))
     if lse is not None:

@@ -93,6 +93,15 @@ int validate(const blockattn_params* p, const int32_t* lens) {
         return fail(BLOCKATTN_ERR_UNSUPPORTED, "num_pages * num_kv_heads must stay below 2^31 (pool slabs are int32)");
     if (!(std::isfinite(p->sm_scale) && p->sm_scale > 0.f))
         return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "sm_scale must be finite and > 0");
+    if (p->kv_dtype != BLOCKATTN_KV_BF16 && p->kv_dtype != BLOCKATTN_KV_FP8_E4M3)
+        return fail(BLOCKATTN_ERR_UNSUPPORTED, "kv_dtype must be BLOCKATTN_KV_BF16 (0) or BLOCKATTN_KV_FP8_E4M3 (1)");
+    if (!(std::isfinite(p->k_scale) && p->k_scale > 0.f))
+        return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "k_scale must be finite and > 0 (1 for an unscaled cache)");
+    if (!std::isfinite(p->v_scale))
+        return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "v_scale must be finite (1 for an unscaled cache)");
+    if (!(std::isfinite((double)p->sm_scale * p->k_scale * 1.4426950408889634) &&
+          (float)((double)p->sm_scale * p->k_scale * 1.4426950408889634) > 0.f))
+        return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "sm_scale * k_scale must stay a finite, non-zero fp32 value");
     if (p->window_left == 0 || p->window_left < -1)
         return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "window_left must be -1 (unwindowed) or >= 1 keys");
     if (p->window_right < -1) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "window_right must be >= -1");
@@ -178,6 +187,7 @@ int build_plan(const blockattn_params* p, const int32_t* lens, blockattn_plan_s*
     pl->R = p->block_size * pl->g;
     pl->NB = (pl->R + 15) / 16;
     pl->shape = choose_shape(p->head_dim, pl->NB, pl->R, p->waves_override);
+    pl->shape.fp8 = p->kv_dtype == BLOCKATTN_KV_FP8_E4M3;
     pl->merge_active = pl->kind == 1 && p->block_size > 1 && p->window_right != 0;
 
     const int B = p->batch, H = p->num_kv_heads;
@@ -280,8 +290,8 @@ int run_forward(blockattn_plan_t plan, const void* q, const void* k, const void*
 
     KernelArgs ka{};
     ka.q = static_cast<const uint16_t*>(q);
-    ka.kc = static_cast<const uint16_t*>(k);
-    ka.vc = static_cast<const uint16_t*>(v);
+    ka.kc = k;
+    ka.vc = v;
     ka.page_table = pt;
     ka.seq_lens = lens;
     ka.work = reinterpret_cast<const WorkItem*>(base + plan->lay.work);
@@ -305,7 +315,9 @@ int run_forward(blockattn_plan_t plan, const void* q, const void* k, const void*
     ka.row_waves = plan->shape.row_waves;
     ka.token_groups = plan->shape.token_groups;
     ka.uniform_splits = plan->uniform_splits;
-    ka.scale_log2 = (float)((double)p.sm_scale * 1.4426950408889634);
+    // A stored key stands for k_scale * k: the logits take k_scale with sm_scale.
+    ka.scale_log2 = (float)((double)p.sm_scale * p.k_scale * 1.4426950408889634);
+    ka.v_scale = p.v_scale;
 
     hipError_t e = hipSuccess;
     if (plan->prof_before) e = hipEventRecord(plan->prof_before, st);

@@ -1,4 +1,5 @@
-// gfx950 kernels for draft-block paged attention.
+// gfx950 kernels for draft-block paged attention (templates; instantiated per KV element type by
+// kernels_bf16.hip and kernels_fp8.hip).
 //
 // Attention kernels (split-KV attention and its epilogue). One workgroup = one
 // work unit: a range of 32-token key tiles of one (request b, kv head). Per tile:
@@ -39,9 +40,13 @@
 // PR #16150 (paged DFlash cross-attention, commits "rework flash-decoding style"
 // and "split count as a runtime argument") and the multi-CTA split-KV of
 // PR #20374, redone for 64-wide wavefronts, MFMA tiles and HND pages.
+#pragma once
+
 #include "internal.h"
 
 #include <math.h>
+
+#include <type_traits>
 
 namespace blockattn {
 namespace {
@@ -83,6 +88,30 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_floa
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 __device__ __forceinline__ u32x4_t ldg16(const uint16_t* p) { return *(const u32x4_t*)p; }
+
+// Eight consecutive K or V elements starting at element `e` of a pool: 16 bytes of
+// bf16, or 8 bytes of fp8 E4M3.
+template <bool FP8>
+using Raw8 = typename std::conditional<FP8, u32x2_t, u32x4_t>::type;
+
+template <bool FP8>
+__device__ __forceinline__ Raw8<FP8> ldkv8(const void* pool, size_t e) {
+    if constexpr (FP8)
+        return *(const u32x2_t*)(static_cast<const uint8_t*>(pool) + e);
+    else
+        return *(const u32x4_t*)(static_cast<const uint16_t*>(pool) + e);
+}
+
+// Eight elements as bf16 (exact: every E4M3 value is a bf16 value).
+__device__ __forceinline__ u32x4_t widen8(u32x4_t v) { return v; }
+__device__ __forceinline__ u32x4_t widen8(u32x2_t v) {
+    const auto c0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false);
+    const auto c1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true);
+    const auto c2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false);
+    const auto c3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true);
+    return u32x4_t{__builtin_bit_cast(uint32_t, c0), __builtin_bit_cast(uint32_t, c1), __builtin_bit_cast(uint32_t, c2),
+                   __builtin_bit_cast(uint32_t, c3)};
+}
 
 // Transposing LDS read (ds_read_b64_tr_b16). Within each 16-lane group, lane l
 // receives element l % 4 of the 8 bytes addressed by lane 4e + (l % 16) / 4, for
@@ -274,10 +303,13 @@ __device__ __forceinline__ void store_rows(const KernelArgs& a, const Unit& u, i
                                            float m, float l, int quad) {
     constexpr int DB = D / 16;
     if (r >= a.R) return;
+    f32x4_t acc_s[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc_s[db] = acc[db] * a.v_scale;  // a stored value stands for v_scale * v
     if (!final) {
         const size_t pr = (size_t)blockIdx.x * a.R + r;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) *(f32x4_t*)(a.part_acc + pr * D + db * 16 + quad * 4) = acc[db];
+        for (int db = 0; db < DB; ++db) *(f32x4_t*)(a.part_acc + pr * D + db * 16 + quad * 4) = acc_s[db];
         if (quad == 0) {
             a.part_m[pr] = m;
             a.part_l[pr] = l;
@@ -288,11 +320,11 @@ __device__ __forceinline__ void store_rows(const KernelArgs& a, const Unit& u, i
     const size_t orow = (size_t)(u.b * a.K + i) * a.Hq + h;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-        const uint32_t lo = f32_to_bf16_rne(acc[db][0]) | ((uint32_t)f32_to_bf16_rne(acc[db][1]) << 16);
-        const uint32_t hi = f32_to_bf16_rne(acc[db][2]) | ((uint32_t)f32_to_bf16_rne(acc[db][3]) << 16);
+        const uint32_t lo = f32_to_bf16_rne(acc_s[db][0]) | ((uint32_t)f32_to_bf16_rne(acc_s[db][1]) << 16);
+        const uint32_t hi = f32_to_bf16_rne(acc_s[db][2]) | ((uint32_t)f32_to_bf16_rne(acc_s[db][3]) << 16);
         *(u32x2_t*)(a.out + orow * D + db * 16 + quad * 4) = u32x2_t{lo, hi};
     }
-    if (quad == 0 && a.lse) a.lse[orow] = l > 0.f ? m + log2f(l) : kNegInf;
+    if (quad == 0 && a.lse) a.lse[orow] = l == 0.f ? kNegInf : m + log2f(l);  // a NaN sum stays NaN
 }
 
 // Epilogue of a unit: merge the token groups' softmax states, then write the
@@ -315,7 +347,7 @@ __device__ void finish_unit(const KernelArgs& a, const Unit& u, WaveRows<D, NBW,
         for (int n = 0; n < NBW; ++n) {
             if (!ALL_ON && !w.on[n]) continue;
             const float l = w.l[n];
-            const float inv = final && l > 0.f ? 1.f / l : (final ? 0.f : 1.f);
+            const float inv = final ? (l == 0.f ? 0.f : 1.f / l) : 1.f;  // no keys: zeros; a NaN sum stays NaN
 #pragma unroll
             for (int db = 0; db < DB; ++db) w.acc[n][db] *= inv;
             store_rows<D>(a, u, (wr * NBW + n) * 16 + r16, final, w.acc[n], w.m[n], l, quad);
@@ -340,14 +372,14 @@ __device__ void finish_unit(const KernelArgs& a, const Unit& u, WaveRows<D, NBW,
         const int srow = (wr * NBW + n) * 16 + r16;
         float M = kNegInf;
         for (int t = 0; t < WT; ++t) M = fmaxf(M, ml[((size_t)t * slots * 16 + srow) * 2]);
+        // A group with no keys (m = -inf) weighs 0; 0 * NaN still carries a NaN sum through.
         float L = 0.f;
-        if (M != kNegInf)
-            for (int t = 0; t < WT; ++t) {
-                const float* e = ml + ((size_t)t * slots * 16 + srow) * 2;
-                L += fast_exp2(e[0] - M) * e[1];
-            }
+        for (int t = 0; t < WT; ++t) {
+            const float* e = ml + ((size_t)t * slots * 16 + srow) * 2;
+            L += (e[0] == kNegInf ? 0.f : fast_exp2(e[0] - M)) * e[1];
+        }
         float alpha = w.m[n] == kNegInf ? 0.f : fast_exp2(w.m[n] - M);
-        if (final) alpha = L > 0.f ? alpha / L : 0.f;
+        if (final) alpha = L == 0.f ? 0.f : alpha / L;
 #pragma unroll
         for (int db = 0; db < DB; ++db) w.acc[n][db] *= alpha;
         rowM[n] = M;
@@ -381,7 +413,7 @@ __device__ void finish_unit(const KernelArgs& a, const Unit& u, WaveRows<D, NBW,
 // global load of the loop sits at a fixed, unconditional place (tile indices past
 // the wave's last tile are clamped to it), which keeps the compiler's wait counts
 // exact: the wait for one tile never drains the tile behind it.
-template <int D, int NBW, bool WINDOWED, bool ALL_ON, int MAXT>
+template <int D, int NBW, bool WINDOWED, bool ALL_ON, int MAXT, bool FP8>
 __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
     constexpr int KK = D / 32, DB = D / 16;
     constexpr int VCH = D / 16;   // 1-KiB chunks of the V tile (16 bytes per lane each)
@@ -407,8 +439,8 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
     const int pmask = (1 << a.p_shift) - 1;
 
     struct TileRegs {
-        u32x4_t k[2][KK];
-        u32x4_t v[VCH];
+        Raw8<FP8> k[2][KK];
+        Raw8<FP8> v[VCH];
     };
 
     for (int win = u.ulo; win < u.uhi; win += kPidWindow) {
@@ -448,13 +480,13 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk)
-                    t.k[mb][kk] = ldg16(a.kc + (mb ? base1 : base0) + (size_t)r16 * D + kk * 32 + quad * 8);
+                    t.k[mb][kk] = ldkv8<FP8>(a.kc, (mb ? base1 : base0) + (size_t)r16 * D + kk * 32 + quad * 8);
 #pragma unroll
             for (int c = 0; c < VCH; ++c) {
                 const int row = c * RPC + (lane * 8) / D;  // tile row of this lane's 16 bytes
                 const int col = (lane * 8) % D;
                 const bool h1 = c * RPC >= 16;
-                t.v[c] = ldg16(a.vc + (h1 ? base1 : base0) + (size_t)(row - (h1 ? 16 : 0)) * D + col);
+                t.v[c] = ldkv8<FP8>(a.vc, (h1 ? base1 : base0) + (size_t)(row - (h1 ? 16 : 0)) * D + col);
             }
         };
 
@@ -467,21 +499,21 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
                     for (int c = 0; c < VCH; ++c) {
                         const int row = c * RPC + (lane * 8) / D;
                         const int col = (lane * 8) % D;
-                        *(u32x4_t*)(vlds + row * VP + col) = (t0 + row < u.N) ? t.v[c] : u32x4_t{0u, 0u, 0u, 0u};
+                        *(u32x4_t*)(vlds + row * VP + col) = (t0 + row < u.N) ? widen8(t.v[c]) : u32x4_t{0u, 0u, 0u, 0u};
                     }
                 } else {
 #pragma unroll
                     for (int c = 0; c < VCH; ++c) {
                         const int row = c * RPC + (lane * 8) / D;
                         const int col = (lane * 8) % D;
-                        *(u32x4_t*)(vlds + row * VP + col) = t.v[c];
+                        *(u32x4_t*)(vlds + row * VP + col) = widen8(t.v[c]);
                     }
                 }
                 bf16x8_t kf[2][KK];
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                    for (int kk = 0; kk < KK; ++kk) kf[mb][kk] = __builtin_bit_cast(bf16x8_t, t.k[mb][kk]);
+                    for (int kk = 0; kk < KK; ++kk) kf[mb][kk] = __builtin_bit_cast(bf16x8_t, widen8(t.k[mb][kk]));
                 w.scores(kf, s);
             }
             if (reissue) issue(t, k + 2);  // the registers are free again: keep two tiles in flight
@@ -527,13 +559,15 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
 // barrier per tile orders the ring; it waits on LDS traffic only, so the DR tiles
 // of global loads stay in flight across it. Loads sit at fixed places (the tile
 // index is clamped past the unit's end), so each wait names exactly one tile.
-template <int D, int NBW, bool WINDOWED, bool ALL_ON, int WR, int DR>
+template <int D, int NBW, bool WINDOWED, bool ALL_ON, int WR, int DR, bool FP8>
 __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared_kernel(const KernelArgs a) {
     constexpr int NT = 64 * WR;
-    constexpr int P8 = D / 8;             // 16-byte pieces per tile row
-    constexpr int NBLK = D / 8;           // 1-KiB blocks per tile (64 pieces each): K and V, 32 rows
+    constexpr int EB = FP8 ? 1 : 2;       // bytes per cached element
+    constexpr int LE = 16 / EB;           // elements per 16-byte lane load
+    constexpr int PL = D / LE;            // lanes per tile row
+    constexpr int NBLK = 2 * T * D / (64 * LE);  // 1-KiB blocks per tile: K and V, 32 rows each
     constexpr int BP = NBLK / 4;          // blocks per 16-row half of K or V
-    constexpr int RPB = 512 / D;          // tile rows per block
+    constexpr int RPB = 64 * LE / D;      // tile rows per block
     constexpr int LPT = (NBLK + WR - 1) / WR;
     constexpr int KP = kKPitch<D>;        // padded row pitch (bf16) of the K tile in LDS
     constexpr int VP = kVPitch<D>;        // and of the V tile
@@ -553,9 +587,9 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
     const int32_t* pt_row = a.page_table + (size_t)u.b * a.stride;
     const int last_page = (u.N - 1) >> a.p_shift;
     const int pmask = (1 << a.p_shift) - 1;
-    // This lane's piece inside any block: row lrow of the block, columns lcol..lcol+7.
-    const int lrow = lane / P8, lcol = (lane % P8) * 8;
-    const uint32_t lane_goff = (uint32_t)(lrow * D + lcol) * 2;   // bytes, in the cache
+    // This lane's piece inside any block: row lrow of the block, columns lcol..lcol+LE-1.
+    const int lrow = lane / PL, lcol = (lane % PL) * LE;
+    const uint32_t lane_goff = (uint32_t)(lrow * D + lcol) * EB;  // bytes, in the cache
     const uint32_t lane_koff = (uint32_t)(lrow * KP + lcol) * 2;  // bytes, in the K tile
     const uint32_t lane_voff = (uint32_t)(lrow * VP + lcol) * 2;  // bytes, in the V tile
 
@@ -603,8 +637,9 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
             for (int k = 0; k < LPT; ++k) {
                 const int b = min(wave + k * WR, NBLK - 1);
                 const int part = b / BP;
-                const uint16_t* base = ((part >> 1) ? a.vc : a.kc) + ((part & 1) ? slab1 : slab0) + (b % BP) * RPB * D;
-                st.c[k] = *(const u32x4_t*)(reinterpret_cast<const char*>(base) + lane_goff);
+                const char* base = static_cast<const char*>((part >> 1) ? a.vc : a.kc) +
+                                   (((part & 1) ? slab1 : slab0) + (size_t)(b % BP) * RPB * D) * EB;
+                st.c[k] = *(const u32x4_t*)(base + lane_goff);
             }
         };
         auto store = [&](const Stage& st, int t, int slot) {
@@ -616,13 +651,24 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
                 const int b = min(wave + k * WR, NBLK - 1);
                 const int part = b / BP;
                 const int row0 = (part & 1) * 16 + (b % BP) * RPB;  // first tile row of the block
-                u32x4_t v = st.c[k];
+                // the lane's LE elements as bf16: one 16-byte piece, or two for fp8
+                u32x4_t v0, v1;
+                if constexpr (FP8) {
+                    v0 = widen8(u32x2_t{st.c[k].x, st.c[k].y});
+                    v1 = widen8(u32x2_t{st.c[k].z, st.c[k].w});
+                } else {
+                    v0 = st.c[k];
+                }
                 if (part >> 1) {
                     // V rows past the sequence end become zeros (stale slots may hold NaN)
-                    if (tail && t0 + row0 + lrow >= u.N) v = u32x4_t{0u, 0u, 0u, 0u};
-                    *(u32x4_t*)(dst + (T * KP + row0 * VP) * 2 + lane_voff) = v;
+                    if (tail && t0 + row0 + lrow >= u.N) v0 = v1 = u32x4_t{0u, 0u, 0u, 0u};
+                    char* vd = dst + (T * KP + row0 * VP) * 2 + lane_voff;
+                    *(u32x4_t*)vd = v0;
+                    if constexpr (FP8) *(u32x4_t*)(vd + 16) = v1;
                 } else {
-                    *(u32x4_t*)(dst + row0 * KP * 2 + lane_koff) = v;
+                    char* kd = dst + row0 * KP * 2 + lane_koff;
+                    *(u32x4_t*)kd = v0;
+                    if constexpr (FP8) *(u32x4_t*)(kd + 16) = v1;
                 }
             }
         };
@@ -708,14 +754,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const KernelArgs a) {
     const int d4 = tid % DL, sl = tid / DL;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     float lsum = 0.f;
-    if (M != kNegInf) {
+    // A split with no keys (m = -inf) weighs 0; 0 * NaN still carries a NaN sum through.
 #pragma unroll 4
-        for (int s = sl; s < S; s += SL) {
-            const size_t pr = (size_t)(u0 + s) * a.R + r;
-            const float wgt = fast_exp2(a.part_m[pr] - M);
-            acc += wgt * *(const f32x4_t*)(a.part_acc + pr * D + 4 * d4);
-            lsum += wgt * a.part_l[pr];
-        }
+    for (int s = sl; s < S; s += SL) {
+        const size_t pr = (size_t)(u0 + s) * a.R + r;
+        const float ms = a.part_m[pr];
+        const float wgt = ms == kNegInf ? 0.f : fast_exp2(ms - M);
+        acc += wgt * *(const f32x4_t*)(a.part_acc + pr * D + 4 * d4);
+        lsum += wgt * a.part_l[pr];
     }
     *(f32x4_t*)&red_acc[sl][4 * d4] = acc;
     if (d4 == 0) red_l[sl] = lsum;
@@ -725,9 +771,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const KernelArgs a) {
     if (tid < D) {
         float o = 0.f;
         for (int k = 0; k < SL; ++k) o += red_acc[k][tid];
-        a.out[orow * D + tid] = f32_to_bf16_rne(L > 0.f ? o / L : 0.f);
+        a.out[orow * D + tid] = f32_to_bf16_rne(L == 0.f ? 0.f : o / L);
     }
-    if (tid == 0 && a.lse) a.lse[orow] = L > 0.f ? M + log2f(L) : kNegInf;
+    if (tid == 0 && a.lse) a.lse[orow] = L == 0.f ? kNegInf : M + log2f(L);
 }
 
 template <typename F>
@@ -742,38 +788,38 @@ hipError_t launch_with_lds(F fn, int units, int threads, size_t lds, const Kerne
     return hipGetLastError();
 }
 
-template <int D, int NBW, bool W, bool ALL_ON>
+template <int D, int NBW, bool W, bool ALL_ON, bool FP8>
 hipError_t launch_stream(const KernelShape& s, int units, const KernelArgs& args, hipStream_t stream) {
     static size_t granted = 0;
     constexpr int MAXT = D == 64 ? 512 : 256;  // D = 128 keeps workgroups small so a wave may use 512 registers
-    return launch_with_lds(stream_kernel<D, NBW, W, ALL_ON, MAXT>, units, 64 * s.row_waves * s.token_groups,
+    return launch_with_lds(stream_kernel<D, NBW, W, ALL_ON, MAXT, FP8>, units, 64 * s.row_waves * s.token_groups,
                            s.lds_bytes, args, stream, &granted);
 }
 
 // Tiles in flight per lane: about 96 registers of staged loads for a wave alone on
 // its SIMD (D = 128, two row blocks), 64 where two waves share a SIMD, at most 8.
-constexpr int shared_depth(int D, int NBW, int WR) {
-    const int lpt = (D / 8 + WR - 1) / WR;  // 1-KiB blocks per wave per tile
+constexpr int shared_depth(int D, int NBW, int WR, bool FP8) {
+    const int lpt = ((FP8 ? D / 16 : D / 8) + WR - 1) / WR;  // 1-KiB blocks per wave per tile
     const int dr = ((D == 128 && NBW == 2) ? 24 : 16) / lpt;
     return dr < 2 ? 2 : (dr > 8 ? 8 : dr);
 }
 
-template <int D, int NBW, int WR, bool W, bool ALL_ON>
+template <int D, int NBW, int WR, bool W, bool ALL_ON, bool FP8>
 hipError_t launch_shared(const KernelShape& s, int units, const KernelArgs& args, hipStream_t stream) {
     static size_t granted = 0;
-    return launch_with_lds(shared_kernel<D, NBW, W, ALL_ON, WR, shared_depth(D, NBW, WR)>, units, 64 * WR,
+    return launch_with_lds(shared_kernel<D, NBW, W, ALL_ON, WR, shared_depth(D, NBW, WR, FP8), FP8>, units, 64 * WR,
                            s.lds_bytes, args, stream, &granted);
 }
 
-template <bool W>
+template <bool W, bool FP8>
 hipError_t dispatch(const KernelShape& s, int units, const KernelArgs& args, hipStream_t stream) {
     if (s.shared) {
 #define BA_SHARED(D_, NBW_, WR_)                                                                        \
     if (s.head_dim == D_ && s.nbw == NBW_ && s.row_waves == WR_)                                        \
-        return s.all_on ? launch_shared<D_, NBW_, WR_, W, true>(s, units, args, stream)                 \
-                        : launch_shared<D_, NBW_, WR_, W, false>(s, units, args, stream);
+        return s.all_on ? launch_shared<D_, NBW_, WR_, W, true, FP8>(s, units, args, stream)            \
+                        : launch_shared<D_, NBW_, WR_, W, false, FP8>(s, units, args, stream);
 #define BA_SHARED1(D_, WR_)                                                                             \
-    if (s.head_dim == D_ && s.nbw == 1 && s.row_waves == WR_) return launch_shared<D_, 1, WR_, W, true>(s, units, args, stream);
+    if (s.head_dim == D_ && s.nbw == 1 && s.row_waves == WR_) return launch_shared<D_, 1, WR_, W, true, FP8>(s, units, args, stream);
         BA_SHARED(64, 2, 2)
         BA_SHARED(64, 2, 3)
         BA_SHARED(64, 2, 4)
@@ -792,8 +838,8 @@ hipError_t dispatch(const KernelShape& s, int units, const KernelArgs& args, hip
     }
 #define BA_CASE(D_, NBW_)                                                                               \
     if (s.head_dim == D_ && s.nbw == NBW_)                                                              \
-        return s.all_on ? launch_stream<D_, NBW_, W, true>(s, units, args, stream)                      \
-                        : launch_stream<D_, NBW_, W, false>(s, units, args, stream);
+        return s.all_on ? launch_stream<D_, NBW_, W, true, FP8>(s, units, args, stream)                 \
+                        : launch_stream<D_, NBW_, W, false, FP8>(s, units, args, stream);
     BA_CASE(64, 1)
     BA_CASE(64, 2)
     BA_CASE(128, 1)
@@ -803,33 +849,4 @@ hipError_t dispatch(const KernelShape& s, int units, const KernelArgs& args, hip
 }
 
 }  // namespace
-
-size_t attention_lds_bytes(const KernelShape& s, int R) {
-    (void)R;
-    const int D = s.head_dim;
-    if (s.shared) {
-        const size_t pitches = D == 64 ? kKPitch<64> + kVPitch<64> : kKPitch<128> + kVPitch<128>;
-        const size_t ring = (size_t)2 * kTileTokens * pitches * sizeof(uint16_t) + 2 * kPidWindow * sizeof(int);
-        const size_t epi = epilogue_floats(D, s.row_waves * s.nbw, 1) * sizeof(float);
-        return ring > epi ? ring : epi;
-    }
-    const size_t vpitch = D == 64 ? kVPitch<64> : kVPitch<128>;
-    const size_t loop = ((size_t)s.token_groups * s.row_waves * kTileTokens) * vpitch * sizeof(uint16_t) +
-                        2 * kPidWindow * sizeof(int);
-    const size_t epi = epilogue_floats(D, s.row_waves * s.nbw, s.token_groups) * sizeof(float);
-    return loop > epi ? loop : epi;
-}
-
-hipError_t launch_attention(const KernelShape& shape, bool windowed, int units, const KernelArgs& args,
-                            hipStream_t stream) {
-    return windowed ? dispatch<true>(shape, units, args, stream) : dispatch<false>(shape, units, args, stream);
-}
-
-hipError_t launch_combine(int head_dim, int rows, const KernelArgs& args, hipStream_t stream) {
-    if (head_dim == 64) hipLaunchKernelGGL(combine_kernel<64>, dim3(rows), dim3(256), 0, stream, args);
-    else if (head_dim == 128) hipLaunchKernelGGL(combine_kernel<128>, dim3(rows), dim3(256), 0, stream, args);
-    else return hipErrorInvalidValue;
-    return hipGetLastError();
-}
-
 }  // namespace blockattn

@@ -1,4 +1,4 @@
-// Internal interface between the host plan/C ABI (api.cpp) and the gfx950 kernels (kernels.hip).
+// Internal interface between the host plan/C ABI (api.cpp) and the gfx950 kernels (kernels_*.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -20,8 +20,8 @@ struct WorkItem {
 
 struct KernelArgs {
     const uint16_t* q;
-    const uint16_t* kc;
-    const uint16_t* vc;
+    const void* kc;        // K pool: bf16 or fp8 E4M3 elements
+    const void* vc;        // V pool
     const int32_t* page_table;
     const int32_t* seq_lens;
     const WorkItem* work;
@@ -38,7 +38,8 @@ struct KernelArgs {
     int32_t row_waves;     // WR: waves streaming the same tiles, each owning NBW row blocks
     int32_t token_groups;  // WT: tile streams per workgroup
     int32_t uniform_splits;  // > 0: every (b, h_kv) has this many splits, unit = pair * S + s (no work list read)
-    float scale_log2;      // sm_scale * log2(e)
+    float scale_log2;      // sm_scale * k_scale * log2(e)
+    float v_scale;         // applied to the outputs (a stored value stands for v_scale * v)
 };
 
 // Chosen kernel shape for a plan.
@@ -49,6 +50,7 @@ struct KernelShape {
     int row_waves;     // WR: waves streaming the same tiles, each owning nbw row blocks
     int token_groups;  // WT
     bool shared;       // row_waves > 1: the workgroup loads each tile once into an LDS ring (shared_kernel)
+    bool fp8;          // K and V pools hold fp8 E4M3 bytes
     int waves_per_simd;  // occupancy the kernel's register use allows (1 or 2)
     size_t lds_bytes;  // dynamic LDS per workgroup
 };
@@ -57,6 +59,9 @@ size_t attention_lds_bytes(const KernelShape& s, int R);
 
 hipError_t launch_attention(const KernelShape& shape, bool windowed, int units, const KernelArgs& args,
                             hipStream_t stream);
+// fp8 E4M3 KV instantiations (kernels_fp8.hip); launch_attention routes to it when shape.fp8.
+hipError_t launch_attention_fp8(const KernelShape& shape, bool windowed, int units, const KernelArgs& args,
+                                hipStream_t stream);
 hipError_t launch_combine(int head_dim, int rows, const KernelArgs& args, hipStream_t stream);
 
 }  // namespace blockattn

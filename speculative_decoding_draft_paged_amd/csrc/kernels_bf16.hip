@@ -1,0 +1,35 @@
+// bf16 KV instantiations of the attention kernels, the split combine and the LDS sizing.
+#include "attention_kernels.h"
+
+namespace blockattn {
+
+size_t attention_lds_bytes(const KernelShape& s, int R) {
+    (void)R;
+    const int D = s.head_dim;
+    if (s.shared) {
+        const size_t pitches = D == 64 ? kKPitch<64> + kVPitch<64> : kKPitch<128> + kVPitch<128>;
+        const size_t ring = (size_t)2 * kTileTokens * pitches * sizeof(uint16_t) + 2 * kPidWindow * sizeof(int);
+        const size_t epi = epilogue_floats(D, s.row_waves * s.nbw, 1) * sizeof(float);
+        return ring > epi ? ring : epi;
+    }
+    const size_t vpitch = D == 64 ? kVPitch<64> : kVPitch<128>;
+    const size_t loop = ((size_t)s.token_groups * s.row_waves * kTileTokens) * vpitch * sizeof(uint16_t) +
+                        2 * kPidWindow * sizeof(int);
+    const size_t epi = epilogue_floats(D, s.row_waves * s.nbw, s.token_groups) * sizeof(float);
+    return loop > epi ? loop : epi;
+}
+
+hipError_t launch_attention(const KernelShape& shape, bool windowed, int units, const KernelArgs& args,
+                            hipStream_t stream) {
+    if (shape.fp8) return launch_attention_fp8(shape, windowed, units, args, stream);
+    return windowed ? dispatch<true, false>(shape, units, args, stream) : dispatch<false, false>(shape, units, args, stream);
+}
+
+hipError_t launch_combine(int head_dim, int rows, const KernelArgs& args, hipStream_t stream) {
+    if (head_dim == 64) hipLaunchKernelGGL(combine_kernel<64>, dim3(rows), dim3(256), 0, stream, args);
+    else if (head_dim == 128) hipLaunchKernelGGL(combine_kernel<128>, dim3(rows), dim3(256), 0, stream, args);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace blockattn

@@ -39,7 +39,10 @@ def upload(inputs: synth.Inputs, device="cuda") -> DeviceCase:
     def bf(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
 
-    return DeviceCase(inputs, bf(inputs.q), bf(inputs.k_pool), bf(inputs.v_pool),
+    def kv(a):  # bf16 bits, or fp8 E4M3 bytes kept as uint8
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device) if a.dtype == np.uint8 else bf(a)
+
+    return DeviceCase(inputs, bf(inputs.q), kv(inputs.k_pool), kv(inputs.v_pool),
                       torch.from_numpy(np.ascontiguousarray(inputs.page_table)).to(device),
                       torch.from_numpy(np.ascontiguousarray(inputs.seq_lens)).to(device))
 
@@ -52,7 +55,8 @@ def params_for(dc: DeviceCase, *, window_left=None, window_right=None, splits=0,
                           sm_scale=c.scale if scale is None else scale,
                           window_left=c.window_left if window_left is None else window_left,
                           window_right=c.window_right if window_right is None else window_right,
-                          splits_override=splits, waves_override=waves)
+                          splits_override=splits, waves_override=waves, kv_dtype=c.kv_dtype, k_scale=c.k_scale,
+                          v_scale=c.v_scale)
 
 
 def run(dc: DeviceCase, *, window_left=None, window_right=None, splits=0, plan_lens=None, with_lse=True,
@@ -74,15 +78,17 @@ def run(dc: DeviceCase, *, window_left=None, window_right=None, splits=0, plan_l
     fwd = ba.blockattn_forward if prm.window_left == -1 else ba.blockattn_windowed_forward
     fwd(plan, dc.q, dc.k, dc.v, dc.page_table, dc.seq_lens, ws, out, lse)
     torch.cuda.synchronize()
-    # A second call on the same plan and workspace must give the same bits: nothing a
-    # call leaves in the workspace may leak into the next one.
+    # A second call on the same plan and workspace must give the same bits (compared as
+    # bits, so NaN outputs of NaN inputs compare equal): nothing a call leaves in the
+    # workspace may leak into the next one.
     first = out.clone()
     first_lse = lse.clone() if lse is not None else None
     fwd(plan, dc.q, dc.k, dc.v, dc.page_table, dc.seq_lens, ws, out, lse)
     torch.cuda.synchronize()
-    assert torch.equal(out, first), "second call on the same plan differs"
+    assert torch.equal(out.view(torch.int16), first.view(torch.int16)), "second call on the same plan differs"
     if lse is not None:
-        assert torch.equal(lse, first_lse), "second call on the same plan differs (lse)"
+        assert torch.equal(lse.view(torch.int32), first_lse.view(torch.int32)), \
+            "second call on the same plan differs (lse)"
     info = plan.info()
     if canary:
         assert bool((ws_all[nbytes:] == 0xA5).all()), "workspace guard bytes were overwritten"

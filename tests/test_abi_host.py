@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_struct_layouts_match_header():
     # params: 12 int32 + 1 float = 52 bytes; info: 9 int32 + padding + size_t
-    assert ctypes.sizeof(ba.blockattn_params) == 52
+    assert ctypes.sizeof(ba.blockattn_params) == 64
     assert ctypes.sizeof(ba.blockattn_plan_info_t) == 48
 
 
@@ -117,6 +117,10 @@ def test_workspace_size_grows_with_batch(B):
 @pytest.mark.parametrize("kw,lens,code,needle", [
     (dict(head_dim=96), [100, 100], ba.BLOCKATTN_ERR_UNSUPPORTED, "head_dim"),
     (dict(num_pages=2 ** 30), [100, 100], ba.BLOCKATTN_ERR_UNSUPPORTED, "num_pages * num_kv_heads"),
+    (dict(kv_dtype=7), [100, 100], ba.BLOCKATTN_ERR_UNSUPPORTED, "kv_dtype"),
+    (dict(kv_dtype="fp8_e4m3", k_scale=0.0), [100, 100], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "k_scale"),
+    (dict(k_scale=float("inf")), [100, 100], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "k_scale"),
+    (dict(v_scale=float("nan")), [100, 100], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "v_scale"),
     (dict(page_size=48), [100, 100], ba.BLOCKATTN_ERR_UNSUPPORTED, "page_size"),
     (dict(num_q_heads=7), [100, 100], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "num_q_heads"),
     (dict(block_size=17), [100, 100], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "block_size"),
@@ -145,3 +149,12 @@ def test_forward_refuses_plans_without_workspace_or_wrong_kind():
     rc = lib.blockattn_windowed_forward(vp(plan.handle), one, one, one, one, one, one, one, one, None)
     assert rc == ba.BLOCKATTN_ERR_PLAN_MISMATCH and "blockattn_forward" in ba.blockattn_last_error()
     plan.destroy()
+
+
+def test_fp8_plan_keeps_the_bf16_shape():
+    """The element type changes only the loads: same kernel shape, units and workspace."""
+    for kw in (dict(), dict(head_dim=128, page_size=64, num_q_heads=16, num_kv_heads=1, window_left=4096,
+                            block_size=7)):
+        a = plan_info(params(**kw), [9000, 5000])
+        b = plan_info(params(**kw, kv_dtype="fp8_e4m3", k_scale=0.0625, v_scale=0.0625), [9000, 5000])
+        assert a == b
