@@ -40,6 +40,8 @@ class _Params(ctypes.Structure):
         ("kv_dtype", ctypes.c_int32),
         ("k_scale", ctypes.c_double),
         ("v_scale", ctypes.c_double),
+        ("k_block", ctypes.c_void_p),
+        ("v_block", ctypes.c_void_p),
     ]
 
 
@@ -69,6 +71,8 @@ def _load():
     lib.oracle_bf16_to_double.restype = ctypes.c_double
     lib.oracle_fp8_e4m3_to_double.argtypes = [ctypes.c_uint8]
     lib.oracle_fp8_e4m3_to_double.restype = ctypes.c_double
+    lib.oracle_encode_kv.argtypes = [ctypes.c_int, ctypes.c_float, ctypes.c_uint16]
+    lib.oracle_encode_kv.restype = ctypes.c_uint16
     _lib = lib
     return lib
 
@@ -82,13 +86,15 @@ def default_threads() -> int:
 
 def attention(q, k_pool, v_pool, page_table, seq_lens, *, block_size, num_q_heads, num_kv_heads, head_dim,
               page_size, sm_scale, window_left=-1, window_right=-1, part=PART_ALL, pairs=None, threads=None,
-              kv_dtype="bf16", k_scale=1.0, v_scale=1.0):
+              kv_dtype="bf16", k_scale=1.0, v_scale=1.0, k_block=None, v_block=None):
     """Return (out [B,K,Hq,D] float64, lse2 [B,K,Hq] float64) straight from the definition.
 
     ``q`` holds bf16 bit patterns (uint16); ``k_pool`` and ``v_pool`` hold bf16
     bits (uint16) or OCP fp8 e4m3 bytes (uint8, ``kv_dtype="fp8_e4m3"``) that
-    stand for ``k_scale`` / ``v_scale`` times their value. ``pairs`` optionally
-    restricts the work to a list of (b, h_kv); other rows are NaN.
+    stand for ``k_scale`` / ``v_scale`` times their value. ``k_block`` /
+    ``v_block`` (bf16 bits [B, K, Hkv, D], both or neither) replace the cache as the
+    source of the K block keys. ``pairs`` optionally restricts the work to a list
+    of (b, h_kv); other rows are NaN.
     """
     lib = _load()
     code = _KV_CODES[kv_dtype]
@@ -99,9 +105,17 @@ def attention(q, k_pool, v_pool, page_table, seq_lens, *, block_size, num_q_head
     page_table = np.ascontiguousarray(page_table, dtype=np.int32)
     seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
     B = int(seq_lens.shape[0])
+    if (k_block is None) != (v_block is None):
+        raise ValueError("k_block and v_block go together")
+    if k_block is not None:
+        k_block = np.ascontiguousarray(k_block, dtype=np.uint16)
+        v_block = np.ascontiguousarray(v_block, dtype=np.uint16)
+        if k_block.shape != (B, block_size, num_kv_heads, head_dim) or v_block.shape != k_block.shape:
+            raise ValueError("block arrays must be [B, K, Hkv, D]")
     prm = _Params(B, block_size, num_q_heads, num_kv_heads, head_dim, page_size, int(page_table.shape[1]),
                   int(k_pool.shape[0]), window_left, window_right, float(sm_scale), code, float(k_scale),
-                  float(v_scale))
+                  float(v_scale), None if k_block is None else k_block.ctypes.data,
+                  None if v_block is None else v_block.ctypes.data)
     out = np.full((B, block_size, num_q_heads, head_dim), np.nan)
     lse2 = np.full((B, block_size, num_q_heads), np.nan)
     if pairs is not None:
@@ -117,7 +131,8 @@ def attention(q, k_pool, v_pool, page_table, seq_lens, *, block_size, num_q_head
     return out, lse2
 
 
-def attention_case(inputs, *, part=PART_ALL, pairs=None, threads=None, window_left=None, window_right=None):
+def attention_case(inputs, *, part=PART_ALL, pairs=None, threads=None, window_left=None, window_right=None,
+                   k_block=None, v_block=None):
     """Oracle on a ``synth.Inputs`` object with the case's own parameters."""
     c = inputs.case
     return attention(inputs.q, inputs.k_pool, inputs.v_pool, inputs.page_table, inputs.seq_lens,
@@ -126,7 +141,7 @@ def attention_case(inputs, *, part=PART_ALL, pairs=None, threads=None, window_le
                      window_left=c.window_left if window_left is None else window_left,
                      window_right=c.window_right if window_right is None else window_right,
                      part=part, pairs=pairs, threads=threads, kv_dtype=c.kv_dtype, k_scale=c.k_scale,
-                     v_scale=c.v_scale)
+                     v_scale=c.v_scale, k_block=k_block, v_block=v_block)
 
 
 def merge(out_a, lse_a, out_b, lse_b):
@@ -151,3 +166,8 @@ def bf16_to_double(bits: int) -> float:
 
 def fp8_e4m3_to_double(code: int) -> float:
     return float(_load().oracle_fp8_e4m3_to_double(code))
+
+
+def encode_kv(kv_dtype: str, scale: float, bits: int) -> int:
+    """The cache element appending bf16 `bits` stores in a `kv_dtype` pool with `scale`."""
+    return int(_load().oracle_encode_kv(_KV_CODES[kv_dtype], float(scale), int(bits)))

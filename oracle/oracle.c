@@ -36,6 +36,12 @@
  *    request b is slot j mod P of page page_table[b, j / P]; a pool is
  *    [pages, Hkv, P, D]. Query head h reads kv head h / (Hq / Hkv).
  *
+ *  - The dense block (TensorRT-LLM PR #16150, the DFlash context kernel fuses the
+ *    dense suffix of block keys into the same softmax as the paged context; its
+ *    "fused block K/V append" writes them into the pages). With k_block / v_block
+ *    given, the K block keys are read from those bf16 arrays instead of the cache;
+ *    the key set does not change.
+ *
  *  - fp8 context storage (TensorRT-LLM PR #16150, paged DFlash context read from
  *    the target KV cache manager's pool: the kernel supports fp8 context storage,
  *    with bf16 dots and fp32 accumulation). The pages fix no format; read here as
@@ -62,6 +68,39 @@ double oracle_fp8_e4m3_to_double(uint8_t code) {
     if (e == 15 && m == 7) return NAN;
     const double v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
     return sign ? -v : v;
+}
+
+uint16_t oracle_encode_kv(int kv_dtype, float scale, uint16_t bits) {
+    const float x = (float)oracle_bf16_to_double(bits);
+    const float q = x / scale; /* IEEE fp32 division */
+    if (kv_dtype == ORACLE_KV_FP8_E4M3) {
+        /* nearest E4M3 value, ties to the even code, by search over the finite codes */
+        if (isnan(q)) return 0x7F;
+        const double a = fabs((double)q);
+        const uint16_t sign = signbit(q) ? 0x80 : 0x00;
+        if (a >= 448.0) return sign | 0x7E;
+        int best = 0;
+        double best_err = INFINITY;
+        for (int c = 0; c <= 0x7E; ++c) {
+            const double err = fabs(oracle_fp8_e4m3_to_double((uint8_t)c) - a);
+            if (err < best_err || (err == best_err && (c & 1) == 0)) {
+                best = c;
+                best_err = err;
+            }
+        }
+        return sign | (uint16_t)best;
+    }
+    /* bf16 of q by round-to-nearest-even: the nearest bf16 above or below */
+    if (isnan(q)) return 0x7FC0;
+    uint32_t u;
+    memcpy(&u, &q, sizeof u);
+    const uint16_t lo = (uint16_t)(u >> 16), hi = (uint16_t)(lo + 1);
+    const double dq = (double)q, dlo = oracle_bf16_to_double(lo), dhi = oracle_bf16_to_double(hi);
+    if ((u & 0xFFFFu) == 0) return lo;
+    const double elo = fabs(dq - dlo), ehi = fabs(dhi - dq);
+    if (elo < ehi) return lo;
+    if (ehi < elo) return hi;
+    return (lo & 1) ? hi : lo;
 }
 
 /* Element d of a K or V row, decoded and scaled. */
@@ -120,9 +159,14 @@ static void one_row(oracle_job* job, int b, int i, int h, double* s) {
 
     double m = -INFINITY;
     for (int64_t j = lo; j <= hi; ++j) {
-        const int64_t kr = key_row(prm, job->pt, b, hk, j);
         double dot = 0.0;
-        for (int d = 0; d < D; ++d) dot += qd[d] * kv_elem(prm, job->k, kr, d, prm->k_scale);
+        if (prm->k_block && j >= n - K) {
+            const uint16_t* kb = prm->k_block + (((int64_t)b * K + (j - (n - K))) * prm->num_kv_heads + hk) * D;
+            for (int d = 0; d < D; ++d) dot += qd[d] * oracle_bf16_to_double(kb[d]);
+        } else {
+            const int64_t kr = key_row(prm, job->pt, b, hk, j);
+            for (int d = 0; d < D; ++d) dot += qd[d] * kv_elem(prm, job->k, kr, d, prm->k_scale);
+        }
         s[j - lo] = prm->sm_scale * dot;
         if (s[j - lo] > m) m = s[j - lo];
     }
@@ -132,8 +176,13 @@ static void one_row(oracle_job* job, int b, int i, int h, double* s) {
     for (int64_t j = lo; j <= hi; ++j) {
         const double e = exp(s[j - lo] - m);
         z += e;
-        const int64_t vr = key_row(prm, job->pt, b, hk, j);
-        for (int d = 0; d < D; ++d) acc[d] += e * kv_elem(prm, job->v, vr, d, prm->v_scale);
+        if (prm->v_block && j >= n - K) {
+            const uint16_t* vb = prm->v_block + (((int64_t)b * K + (j - (n - K))) * prm->num_kv_heads + hk) * D;
+            for (int d = 0; d < D; ++d) acc[d] += e * oracle_bf16_to_double(vb[d]);
+        } else {
+            const int64_t vr = key_row(prm, job->pt, b, hk, j);
+            for (int d = 0; d < D; ++d) acc[d] += e * kv_elem(prm, job->v, vr, d, prm->v_scale);
+        }
     }
     for (int d = 0; d < D; ++d) o[d] = acc[d] / z;
     job->lse2[row] = (m + log(z)) / log(2.0);
@@ -165,6 +214,7 @@ int oracle_attention(const oracle_params* prm, int part, const uint16_t* q, cons
     if (part < ORACLE_PART_ALL || part > ORACLE_PART_FUTURE) return -1;
     if (prm->kv_dtype != ORACLE_KV_BF16 && prm->kv_dtype != ORACLE_KV_FP8_E4M3) return -1;
     if (!isfinite(prm->k_scale) || !isfinite(prm->v_scale)) return -1;
+    if ((prm->k_block == NULL) != (prm->v_block == NULL)) return -1;
     if (prm->window_left == 0 || prm->window_left < -1 || prm->window_right < -1) return -1;
 
     int64_t max_keys = 0;

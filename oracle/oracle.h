@@ -29,6 +29,9 @@ typedef struct oracle_params {
     int32_t kv_dtype;          /* ORACLE_KV_BF16 or ORACLE_KV_FP8_E4M3: element type of both pools */
     double k_scale;            /* a stored key element stands for k_scale times its decoded value */
     double v_scale;            /* likewise for values */
+    const uint16_t* k_block;   /* NULL, or bf16 bits [B, K, Hkv, D]: the block's keys, read from here (as
+                                  they are, no scale) instead of the cache for positions N_b - K .. N_b - 1 */
+    const uint16_t* v_block;   /* likewise for values; given together with k_block */
 } oracle_params;
 
 enum { ORACLE_KV_BF16 = 0, ORACLE_KV_FP8_E4M3 = 1 };
@@ -59,6 +62,14 @@ double oracle_bf16_to_double(uint16_t bits);
 
 /* Exact OCP fp8 e4m3 -> double decoding used by the oracle (exported for its tests). */
 double oracle_fp8_e4m3_to_double(uint8_t code);
+
+/*
+ * The cache element that appending the bf16 value `bits` to a pool of kv_dtype with
+ * `scale` stores: q = fp32(value) / fp32(scale) in IEEE fp32 (correctly rounded),
+ * then bf16 or OCP E4M3 by round-to-nearest-even; E4M3 saturates at +-448 and maps
+ * NaN to 0x7F. Returns the bf16 bits or the E4M3 byte.
+ */
+uint16_t oracle_encode_kv(int kv_dtype, float scale, uint16_t bits);
 
 #ifdef __cplusplus
 }

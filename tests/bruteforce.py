@@ -51,8 +51,9 @@ def key_mask(n: int, K: int, g: int, window_left: int, window_right: int, part: 
     return m
 
 
-def attention(inputs, window_left=None, window_right=None, part="all"):
-    """Dense masked attention for every row; returns (out, lse2) like the oracle."""
+def attention(inputs, window_left=None, window_right=None, part="all", k_block=None, v_block=None):
+    """Dense masked attention for every row; returns (out, lse2) like the oracle. With k_block / v_block
+    (bf16 bits [B, K, Hkv, D]) the last K keys of each request come from them instead of the cache."""
     c = inputs.case
     wl = c.window_left if window_left is None else window_left
     wr = c.window_right if window_right is None else window_right
@@ -66,6 +67,9 @@ def attention(inputs, window_left=None, window_right=None, part="all"):
         n = int(inputs.seq_lens[b])
         kd = dense_kv(inputs.k_pool, inputs.page_table, b, n, c.k_scale)
         vd = dense_kv(inputs.v_pool, inputs.page_table, b, n, c.v_scale)
+        if k_block is not None:
+            kd[n - K:] = bf16_bits_to_float(k_block[b]).astype(np.float64)
+            vd[n - K:] = bf16_bits_to_float(v_block[b]).astype(np.float64)
         mask = key_mask(n, K, g, wl, wr, part)
         for hk in range(Hkv):
             qr = q[b, :, hk * g:(hk + 1) * g, :].reshape(K * g, D)
