@@ -160,6 +160,31 @@ int blockattn_windowed_forward(blockattn_plan_t plan, const void* q, const void*
                                const int32_t* page_table, const int32_t* seq_lens, void* workspace, void* out,
                                float* lse, void* stream);
 
+/*
+ * Block attention with the block's own keys and values given as dense bf16
+ * arrays, either plan kind (TensorRT-LLM PR #16150: the paged DFlash context
+ * kernel fuses the dense suffix of block keys into the same softmax, and the
+ * K/V of the block are appended to the cache just before attention).
+ *   k_block, v_block  bf16 [B, K, Hkv, D]: the keys and values at positions
+ *                     C_b .. C_b + K - 1, read from here instead of the cache
+ *                     (unscaled); the key set is the same as the plan kind's.
+ *   append            0: the cache is only read (its block slots may hold
+ *                     anything). 1: the call also stores the block into its
+ *                     cache slots (page_table[b, j / P], slot j % P), each element
+ *                     as fp32(x) / fp32(scale) rounded to the pool's type (bf16,
+ *                     or E4M3 by nearest-even saturating at +-448), so the next
+ *                     step finds it there.
+ * Other arguments as for blockattn_forward / blockattn_windowed_forward (lse
+ * required for a windowed plan). k_cache and v_cache are written only with
+ * append = 1, and only at the block slots. Requires v_scale != 0 with a finite
+ * fp32 reciprocal (the block values join the scaled cache values as v / v_scale:
+ * each probability of a block key is multiplied by 1 / v_scale before its bf16
+ * rounding, which is exact when v_scale is a power of two).
+ */
+int blockattn_forward_block(blockattn_plan_t plan, const void* q, const void* k_block, const void* v_block,
+                            void* k_cache, void* v_cache, const int32_t* page_table, const int32_t* seq_lens,
+                            void* workspace, void* out, float* lse, int32_t append, void* stream);
+
 /* Describe the plan (path taken, units, splits, future block keys on or off). */
 int blockattn_plan_info(blockattn_plan_t plan, blockattn_plan_info_t* info);
 

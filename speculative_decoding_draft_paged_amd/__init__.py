@@ -34,6 +34,7 @@ EXPORTED = (
     "blockattn_plan",
     "blockattn_forward",
     "blockattn_windowed_forward",
+    "blockattn_forward_block",
     "blockattn_plan_info",
     "blockattn_plan_set_profile_events",
     "blockattn_plan_destroy",
@@ -108,13 +109,14 @@ def load_library():
     fwd = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.blockattn_forward.argtypes = fwd
     lib.blockattn_windowed_forward.argtypes = fwd
+    lib.blockattn_forward_block.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp]
     lib.blockattn_plan_info.argtypes = [vp, ctypes.POINTER(blockattn_plan_info_t)]
     lib.blockattn_plan_set_profile_events.argtypes = [vp, vp, vp]
     lib.blockattn_plan_destroy.argtypes = [vp]
     lib.blockattn_plan_destroy.restype = None
     lib.blockattn_last_error.restype = ctypes.c_char_p
-    for name in ("blockattn_workspace_size", "blockattn_plan", "blockattn_forward",
-                 "blockattn_windowed_forward", "blockattn_plan_info", "blockattn_plan_set_profile_events"):
+    for name in ("blockattn_workspace_size", "blockattn_plan", "blockattn_forward", "blockattn_windowed_forward",
+                 "blockattn_forward_block", "blockattn_plan_info", "blockattn_plan_set_profile_events"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -281,3 +283,18 @@ def blockattn_windowed_forward(plan: Plan, q, k_cache, v_cache, page_table, seq_
     """Non-causal windowed block attention: causal windowed decode + future-key merge (launch only)."""
     _forward("blockattn_windowed_forward", plan, q, k_cache, v_cache, page_table, seq_lens, workspace, out, lse,
              stream)
+
+
+def blockattn_forward_block(plan: Plan, q, k_block, v_block, k_cache, v_cache, page_table, seq_lens, workspace, out,
+                            lse=None, append=False, stream=None):
+    """Block attention with the block's K/V from dense bf16 [B, K, Hkv, D] arrays; optionally append them."""
+    _check_buffers(plan, q, k_cache, v_cache, page_table, seq_lens, out, lse)
+    p = plan.params
+    blk = p.batch * p.block_size * p.num_kv_heads * p.head_dim
+    _expect("k_block", k_block, blk, ("bfloat16", "int16", "uint16"))
+    _expect("v_block", v_block, blk, ("bfloat16", "int16", "uint16"))
+    vp = ctypes.c_void_p
+    _check(load_library().blockattn_forward_block(
+        vp(plan.handle), vp(_ptr(q)), vp(_ptr(k_block)), vp(_ptr(v_block)), vp(_ptr(k_cache)), vp(_ptr(v_cache)),
+        vp(_ptr(page_table)), vp(_ptr(seq_lens)), vp(_ptr(workspace)), vp(_ptr(out)), vp(_ptr(lse)),
+        ctypes.c_int32(1 if append else 0), vp(_stream(stream))))

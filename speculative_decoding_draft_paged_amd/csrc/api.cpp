@@ -283,12 +283,17 @@ int check_forward(blockattn_plan_t plan, int kind, const void* q, const void* k,
 }
 
 int run_forward(blockattn_plan_t plan, const void* q, const void* k, const void* v, const int32_t* pt,
-                const int32_t* lens, void* ws, void* out, float* lse, void* stream) {
+                const int32_t* lens, void* ws, void* out, float* lse, void* stream, const void* k_block = nullptr,
+                const void* v_block = nullptr, int append = 0) {
     const blockattn_params& p = plan->prm;
     char* base = static_cast<char*>(ws);
     hipStream_t st = static_cast<hipStream_t>(stream);
 
     KernelArgs ka{};
+    ka.k_block = static_cast<const uint16_t*>(k_block);
+    ka.v_block = static_cast<const uint16_t*>(v_block);
+    ka.append = append ? 1 : 0;
+    ka.k_scale = p.k_scale;
     ka.q = static_cast<const uint16_t*>(q);
     ka.kc = k;
     ka.vc = v;
@@ -318,6 +323,8 @@ int run_forward(blockattn_plan_t plan, const void* q, const void* k, const void*
     // A stored key stands for k_scale * k: the logits take k_scale with sm_scale.
     ka.scale_log2 = (float)((double)p.sm_scale * p.k_scale * 1.4426950408889634);
     ka.v_scale = p.v_scale;
+    ka.block_scale_log2 = (float)((double)p.sm_scale * 1.4426950408889634);
+    ka.block_p_mul = 1.0f / p.v_scale;
 
     hipError_t e = hipSuccess;
     if (plan->prof_before) e = hipEventRecord(plan->prof_before, st);
@@ -406,6 +413,25 @@ int blockattn_windowed_forward(blockattn_plan_t plan, const void* q, const void*
     int rc = check_forward(plan, 1, q, k_cache, v_cache, page_table, seq_lens, workspace, out, lse);
     if (rc) return rc;
     return run_forward(plan, q, k_cache, v_cache, page_table, seq_lens, workspace, out, lse, stream);
+}
+
+int blockattn_forward_block(blockattn_plan_t plan, const void* q, const void* k_block, const void* v_block,
+                            void* k_cache, void* v_cache, const int32_t* page_table, const int32_t* seq_lens,
+                            void* workspace, void* out, float* lse, int32_t append, void* stream) {
+    if (!plan) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "plan is NULL");
+    if (!k_block || !v_block)
+        return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "k_block and v_block (bf16 [B, K, Hkv, D]) are required");
+    // The accumulator is kept in stored units (the epilogue multiplies by v_scale), so
+    // the block's unscaled values join it divided by v_scale.
+    if (!std::isfinite(1.0f / plan->prm.v_scale))
+        return fail(BLOCKATTN_ERR_INVALID_ARGUMENT,
+                    "dense block values need v_scale != 0 with a finite fp32 reciprocal (they join as v / v_scale)");
+    if (!std::isfinite((float)((double)plan->prm.sm_scale * 1.4426950408889634)))
+        return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "sm_scale * log2(e) must stay a finite fp32 value");
+    int rc = check_forward(plan, plan->kind, q, k_cache, v_cache, page_table, seq_lens, workspace, out, lse);
+    if (rc) return rc;
+    return run_forward(plan, q, k_cache, v_cache, page_table, seq_lens, workspace, out, lse, stream, k_block, v_block,
+                       append);
 }
 
 int blockattn_plan_info(blockattn_plan_t plan, blockattn_plan_info_t* info) {

@@ -102,6 +102,26 @@ __device__ __forceinline__ Raw8<FP8> ldkv8(const void* pool, size_t e) {
         return *(const u32x4_t*)(static_cast<const uint16_t*>(pool) + e);
 }
 
+// OCP E4M3 of an fp32 value by round-to-nearest-even, saturating at +-448; NaN -> 0x7F.
+__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float q) {
+    const uint32_t u = __float_as_uint(q);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const float a = fabsf(q);
+    if (a != a) return 0x7Fu;
+    if (a >= 448.f) return sign | 0x7Eu;
+    if (a < 0.015625f) return sign | (uint32_t)__builtin_rintf(a * 512.f);  // below 2^-6: multiples of 2^-9
+    int e = (int)((u >> 23) & 0xFFu) - 127;                                 // -6 .. 8
+    uint32_t m3 = (u >> 20) & 7u;
+    const uint32_t rem = u & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) ++m3;
+    if (m3 == 8u) {
+        m3 = 0;
+        ++e;
+    }
+    if (e > 8 || (e == 8 && m3 == 7u)) return sign | 0x7Eu;
+    return sign | ((uint32_t)(e + 7) << 3) | m3;
+}
+
 // Eight elements as bf16 (exact: every E4M3 value is a bf16 value).
 __device__ __forceinline__ u32x4_t widen8(u32x4_t v) { return v; }
 __device__ __forceinline__ u32x4_t widen8(u32x2_t v) {
@@ -142,8 +162,10 @@ __device__ __forceinline__ float quad_sum(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// N keys, the last K of them the block (p = C + i); NC of them are read from the
+// cache (N, or C when the block comes from dense arrays); tiles [ulo, uhi).
 struct Unit {
-    int b, hk, s, S, N, C, ulo, uhi;
+    int b, hk, s, S, N, C, NC, ulo, uhi;
 };
 
 template <bool WINDOWED>
@@ -165,8 +187,9 @@ __device__ __forceinline__ Unit decode_unit(const KernelArgs& a) {
     u.S = wi.S;
     u.N = clampi(a.seq_lens[wi.b], a.K, a.stride * a.P);
     u.C = u.N - a.K;
+    u.NC = a.k_block ? u.C : u.N;
     const int key_lo = (WINDOWED && a.window_left > 0) ? max(0, u.C - a.window_left + 1) : 0;
-    const int tb = key_lo / T, te = (u.N + T - 1) / T, nt = te - tb;
+    const int tb = key_lo / T, te = max(tb, (u.NC + T - 1) / T), nt = te - tb;
     u.ulo = tb + (int)((int64_t)wi.s * nt / wi.S);
     u.uhi = tb + (int)((int64_t)(wi.s + 1) * nt / wi.S);
     return u;
@@ -183,6 +206,7 @@ struct WaveRows {
     f32x4_t acc[NBW][DB];
     float m[NBW], l[NBW];
     int lo_max, hi_min;
+    int hi_cap;  // keys at or past this come from elsewhere (the dense block) and are masked here
 
     __device__ __forceinline__ void init(const KernelArgs& a, const Unit& u, int first_block, int lane) {
         const int r16 = lane & 15, quad = lane >> 4;
@@ -212,6 +236,7 @@ struct WaveRows {
         }
         lo_max = left_win ? max(0, u.C + a.K - a.window_left) : 0;
         hi_min = WINDOWED ? min(u.N - 1, u.C + right) : u.N - 1;
+        hi_cap = u.NC;
     }
 
     // Scores of one tile for every owned row block.
@@ -237,10 +262,14 @@ struct WaveRows {
     // accumulator rescale is rare and probabilities stay below 2^kRescaleSlack
     // (exact in fp32 and representable in bf16). The softmax scale is folded into
     // the exponent's FMA.
+    // PMUL: the tile's values are in other units than the accumulator's; each
+    // probability is multiplied by pmul (after it joins the row sum) before its bf16
+    // rounding for the P V product.
+    template <bool PMUL = false>
     __device__ __forceinline__ void update(const f32x4_t (&s)[NBW][2], const bf16x8_t (&vf)[DB], int t0, float scale,
-                                           int quad) {
+                                           int quad, float pmul = 1.f) {
         constexpr float kRescaleSlack = 8.f;
-        const bool edge = (t0 < lo_max) || (t0 + T - 1 > hi_min);
+        const bool edge = (t0 < lo_max) || (t0 + T - 1 > hi_min) || (t0 + T > hi_cap);
 #pragma unroll
         for (int n = 0; n < NBW; ++n) {
             if (!ALL_ON && !on[n]) continue;
@@ -255,7 +284,7 @@ struct WaveRows {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int tok = t0 + mb * 16 + quad * 4 + j;
-                        if (tok < row_lo[n] || tok > row_hi[n]) x[mb * 4 + j] = kNegInf;
+                        if (tok < row_lo[n] || tok > row_hi[n] || tok >= hi_cap) x[mb * 4 + j] = kNegInf;
                     }
             }
             float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
@@ -275,7 +304,10 @@ struct WaveRows {
             for (int k = 0; k < 8; ++k) {
                 const float p = fast_exp2(fmaf(x[k], scale, neg_m));
                 psum += p;
-                pb[k] = (__bf16)p;
+                if constexpr (PMUL)
+                    pb[k] = (__bf16)(p * pmul);
+                else
+                    pb[k] = (__bf16)p;
             }
             l[n] += psum;
 #pragma unroll
@@ -405,6 +437,31 @@ __device__ void finish_unit(const KernelArgs& a, const Unit& u, WaveRows<D, NBW,
     }
 }
 
+// Store the block's keys and values (dense bf16 [B, K, Hkv, D]) of this unit's
+// (b, h_kv) into their cache slots C .. C + K - 1, encoded for the pool: the fp32
+// quotient by the pool scale, rounded to bf16 or to saturating E4M3.
+template <int D, bool FP8>
+__device__ void append_block(const KernelArgs& a, const Unit& u) {
+    const int32_t* pt_row = a.page_table + (size_t)u.b * a.stride;
+    const int pmask = (1 << a.p_shift) - 1;
+    const int n = a.K * D;
+    for (int idx = threadIdx.x; idx < 2 * n; idx += blockDim.x) {
+        const bool isv = idx >= n;
+        const int e = isv ? idx - n : idx;
+        const int i = e / D, d = e - (e / D) * D;
+        const int j = u.C + i;
+        const int page = clampi(pt_row[j >> a.p_shift], 0, a.num_pages - 1);
+        const size_t off = (((size_t)page * a.Hkv + u.hk) << (a.p_shift + kLog2<D>)) + (size_t)(j & pmask) * D + d;
+        const uint16_t xb = (isv ? a.v_block : a.k_block)[((size_t)(u.b * a.K + i) * a.Hkv + u.hk) * D + d];
+        const float q = bf16_to_f32(xb) / (isv ? a.v_scale : a.k_scale);
+        void* pool = const_cast<void*>(isv ? a.vc : a.kc);
+        if constexpr (FP8)
+            static_cast<uint8_t*>(pool)[off] = (uint8_t)f32_to_e4m3_sat(q);
+        else
+            static_cast<uint16_t*>(pool)[off] = f32_to_bf16_rne(q);
+    }
+}
+
 // ---------------------------------------------------------------------------------
 // Streaming main loop: one wave owns every row (R <= 16 * NBW), WT waves per
 // workgroup stream interleaved tiles of the unit, two tiles in flight per wave.
@@ -435,7 +492,7 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
     int* pid_tab = reinterpret_cast<int*>(lds + (size_t)WT * WR * T * VP);
 
     const int32_t* pt_row = a.page_table + (size_t)u.b * a.stride;
-    const int last_page = (u.N - 1) >> a.p_shift;
+    const int last_page = max(u.NC - 1, 0) >> a.p_shift;
     const int pmask = (1 << a.p_shift) - 1;
 
     struct TileRegs {
@@ -494,12 +551,12 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
             const int t0 = (win + tg + k * WT) * T;
             f32x4_t s[NBW][2];
             if (valid) {
-                if (t0 + T > u.N) {  // the tail tile: rows past the sequence end become zeros
+                if (t0 + T > u.NC) {  // the tail tile: rows past the cached keys become zeros
 #pragma unroll
                     for (int c = 0; c < VCH; ++c) {
                         const int row = c * RPC + (lane * 8) / D;
                         const int col = (lane * 8) % D;
-                        *(u32x4_t*)(vlds + row * VP + col) = (t0 + row < u.N) ? widen8(t.v[c]) : u32x4_t{0u, 0u, 0u, 0u};
+                        *(u32x4_t*)(vlds + row * VP + col) = (t0 + row < u.NC) ? widen8(t.v[c]) : u32x4_t{0u, 0u, 0u, 0u};
                     }
                 } else {
 #pragma unroll
@@ -546,6 +603,46 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
             consume(tb, k + 1, k + 1 < nk, false);
         }
     }
+    if (a.k_block != nullptr && u.s == u.S - 1) {
+        // The block keys C .. N - 1 (K <= 16 of them) from the dense arrays, as one more
+        // tile at token C, consumed by token group 0; then the optional append.
+        if (tg == 0) {
+            w.hi_cap = u.N;
+            const size_t rstride = (size_t)a.Hkv * D;
+            const uint16_t* kb = a.k_block + ((size_t)u.b * a.K * a.Hkv + u.hk) * D;
+            const uint16_t* vb = a.v_block + ((size_t)u.b * a.K * a.Hkv + u.hk) * D;
+            bf16x8_t kf[2][KK];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) {
+                    const int i = mb * 16 + r16;
+                    kf[mb][kk] = __builtin_bit_cast(bf16x8_t, i < a.K ? ldg16(kb + i * rstride + kk * 32 + quad * 8)
+                                                                     : u32x4_t{0u, 0u, 0u, 0u});
+                }
+#pragma unroll
+            for (int c = 0; c < VCH; ++c) {
+                const int row = c * RPC + (lane * 8) / D;
+                const int col = (lane * 8) % D;
+                *(u32x4_t*)(vlds + row * VP + col) = row < a.K ? ldg16(vb + row * rstride + col) : u32x4_t{0u, 0u, 0u, 0u};
+            }
+            f32x4_t s[NBW][2];
+            w.scores(kf, s);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            bf16x8_t vf[DB];
+            const uint16_t* vrow = vlds + (size_t)(4 * quad + (r16 >> 2)) * VP + 4 * (r16 & 3);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const u32x2_t lo = lds_read_tr16(vrow + db * 16);
+                const u32x2_t hi = lds_read_tr16(vrow + 16 * VP + db * 16);
+                vf[db] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+            }
+            w.template update<true>(s, vf, u.C, a.block_scale_log2, quad, a.block_p_mul);
+        }
+        if (a.append) append_block<D, FP8>(a, u);
+    }
     finish_unit(a, u, w, tg, wr, WT, WR, reinterpret_cast<float*>(lds));
 }
 
@@ -585,7 +682,7 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
     int* pid_tab = reinterpret_cast<int*>(lds + 2 * SLOT);
 
     const int32_t* pt_row = a.page_table + (size_t)u.b * a.stride;
-    const int last_page = (u.N - 1) >> a.p_shift;
+    const int last_page = max(u.NC - 1, 0) >> a.p_shift;
     const int pmask = (1 << a.p_shift) - 1;
     // This lane's piece inside any block: row lrow of the block, columns lcol..lcol+LE-1.
     const int lrow = lane / PL, lcol = (lane % PL) * LE;
@@ -595,6 +692,34 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
 
     struct Stage {
         u32x4_t c[LPT];
+    };
+
+    // Scores, softmax update and PV for the tile at token t0 held in ring slot `slot`.
+    // dense: the tile holds the block's unscaled keys and values from the dense arrays
+    auto compute_at = [&](int t0, int slot, auto dense) {
+        const uint16_t* kl = lds + slot * SLOT;
+        const uint16_t* vl = kl + T * KP;
+        bf16x8_t kf[2][KK];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                kf[mb][kk] =
+                    __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(kl + (mb * 16 + r16) * KP + kk * 32 + quad * 8));
+        f32x4_t s[NBW][2];
+        w.scores(kf, s);
+        bf16x8_t vf[DB];
+        const uint16_t* vrow = vl + (4 * quad + (r16 >> 2)) * VP + 4 * (r16 & 3);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const u32x2_t lo = lds_read_tr16(vrow + db * 16);
+            const u32x2_t hi = lds_read_tr16(vrow + 16 * VP + db * 16);
+            vf[db] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+        }
+        if constexpr (decltype(dense)::value)
+            w.template update<true>(s, vf, t0, a.block_scale_log2, quad, a.block_p_mul);
+        else
+            w.update(s, vf, t0, a.scale_log2, quad);
     };
 
     for (int win = u.ulo; win < u.uhi; win += kPidWindow) {
@@ -644,7 +769,7 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
         };
         auto store = [&](const Stage& st, int t, int slot) {
             const int t0 = (win + t) * T;
-            const bool tail = t0 + T > u.N;
+            const bool tail = t0 + T > u.NC;
             char* dst = reinterpret_cast<char*>(lds + slot * SLOT);
 #pragma unroll
             for (int k = 0; k < LPT; ++k) {
@@ -661,7 +786,7 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
                 }
                 if (part >> 1) {
                     // V rows past the sequence end become zeros (stale slots may hold NaN)
-                    if (tail && t0 + row0 + lrow >= u.N) v0 = v1 = u32x4_t{0u, 0u, 0u, 0u};
+                    if (tail && t0 + row0 + lrow >= u.NC) v0 = v1 = u32x4_t{0u, 0u, 0u, 0u};
                     char* vd = dst + (T * KP + row0 * VP) * 2 + lane_voff;
                     *(u32x4_t*)vd = v0;
                     if constexpr (FP8) *(u32x4_t*)(vd + 16) = v1;
@@ -672,29 +797,7 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
                 }
             }
         };
-        auto compute = [&](int t, int slot) {
-            const int t0 = (win + t) * T;
-            const uint16_t* kl = lds + slot * SLOT;
-            const uint16_t* vl = kl + T * KP;
-            bf16x8_t kf[2][KK];
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk)
-                    kf[mb][kk] = __builtin_bit_cast(
-                        bf16x8_t, *(const u32x4_t*)(kl + (mb * 16 + r16) * KP + kk * 32 + quad * 8));
-            f32x4_t s[NBW][2];
-            w.scores(kf, s);
-            bf16x8_t vf[DB];
-            const uint16_t* vrow = vl + (4 * quad + (r16 >> 2)) * VP + 4 * (r16 & 3);
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const u32x2_t lo = lds_read_tr16(vrow + db * 16);
-                const u32x2_t hi = lds_read_tr16(vrow + 16 * VP + db * 16);
-                vf[db] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
-            }
-            w.update(s, vf, t0, a.scale_log2, quad);
-        };
+        auto compute = [&](int t, int slot) { compute_at((win + t) * T, slot, std::false_type{}); };
 
         // Tile t waits in st[t % DR] until it is written to ring slot t & 1. The
         // scheduling barriers keep the loads of successive tiles in tile order, so the
@@ -720,6 +823,26 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
                 __syncthreads();
             }
         }
+    }
+    if (a.k_block != nullptr && u.s == u.S - 1) {
+        // The block keys C .. N - 1 (K <= 16 of them) from the dense arrays into ring
+        // slot 0 (rows past K zero), consumed as one more tile at token C by every
+        // row-wave; then the optional append.
+        __syncthreads();  // every wave is done with the ring
+        const size_t rstride = (size_t)a.Hkv * D;
+        const size_t b0 = ((size_t)u.b * a.K * a.Hkv + u.hk) * D;
+        for (int idx = tid; idx < 2 * T * (D / 8); idx += NT) {
+            const bool isv = idx >= T * (D / 8);
+            const int e = isv ? idx - T * (D / 8) : idx;
+            const int row = e / (D / 8), col = (e - (e / (D / 8)) * (D / 8)) * 8;
+            const uint16_t* src = (isv ? a.v_block : a.k_block) + b0 + row * rstride + col;
+            *(u32x4_t*)(lds + (isv ? T * KP + row * VP : row * KP) + col) =
+                row < a.K ? ldg16(src) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+        __syncthreads();
+        w.hi_cap = u.N;
+        compute_at(u.C, 0, std::true_type{});
+        if (a.append) append_block<D, FP8>(a, u);
     }
     finish_unit(a, u, w, 0, wave, 1, WR, reinterpret_cast<float*>(lds));
 }

@@ -40,6 +40,13 @@ struct KernelArgs {
     int32_t uniform_splits;  // > 0: every (b, h_kv) has this many splits, unit = pair * S + s (no work list read)
     float scale_log2;      // sm_scale * k_scale * log2(e)
     float v_scale;         // applied to the outputs (a stored value stands for v_scale * v)
+    float k_scale;         // pool scales again, for encoding appended block keys and values
+    const uint16_t* k_block;  // NULL: the block keys are in the cache; else bf16 [B, K, Hkv, D] read instead
+    const uint16_t* v_block;
+    int32_t append;        // with k_block: the last split of each (b, h_kv) also stores the block into the cache
+    float block_scale_log2;  // sm_scale * log2(e): logit scale of the dense block keys (they are unscaled)
+    float block_p_mul;       // 1 / v_scale: the dense block values join the accumulator, which is kept in
+                             // stored units, through probabilities multiplied by this
 };
 
 // Chosen kernel shape for a plan.

@@ -151,6 +151,27 @@ def test_forward_refuses_plans_without_workspace_or_wrong_kind():
     plan.destroy()
 
 
+def test_forward_block_checks_its_own_arguments_first():
+    lib = ba.load_library()
+    vp = ctypes.c_void_p
+    one = vp(0x1000)
+
+    def call(plan, kb, vb, append=0):
+        return lib.blockattn_forward_block(vp(plan.handle), one, kb, vb, one, one, one, one, None, one, one,
+                                           ctypes.c_int32(append), None)
+
+    plan = ba.blockattn_plan(params(), [100, 100])
+    assert call(plan, None, one) == ba.BLOCKATTN_ERR_INVALID_ARGUMENT
+    assert "k_block" in ba.blockattn_last_error()
+    assert call(plan, one, one) == ba.BLOCKATTN_ERR_PLAN_MISMATCH and "workspace" in ba.blockattn_last_error()
+    plan.destroy()
+    for vs in (0.0, 1e-39, -1e-39):  # no finite fp32 reciprocal
+        plan = ba.blockattn_plan(params(kv_dtype="fp8_e4m3", v_scale=vs), [100, 100])
+        assert call(plan, one, one) == ba.BLOCKATTN_ERR_INVALID_ARGUMENT
+        assert "v_scale" in ba.blockattn_last_error()
+        plan.destroy()
+
+
 def test_fp8_plan_keeps_the_bf16_shape():
     """The element type changes only the loads: same kernel shape, units and workspace."""
     for kw in (dict(), dict(head_dim=128, page_size=64, num_q_heads=16, num_kv_heads=1, window_left=4096,
