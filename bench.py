@@ -47,14 +47,24 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kv_bytes(case, seq_lens) -> int:
-    """Algorithmic KV bytes of one call: every key a row needs, read once (K and V, 2 B each for bf16, 1 for fp8)."""
+def kv_bytes(case, seq_lens, block="cache") -> int:
+    """Algorithmic KV bytes of one call: every key a row needs, read once (K and V, 2 B each for bf16, 1 for fp8).
+
+    block "dense": the K block keys and values come from dense bf16 arrays (2 B each) instead of the
+    cache; "append": the same, plus writing them into the cache (K and V, at the cache's element size).
+    """
     eb = 1 if case.kv_dtype == "fp8_e4m3" else 2
+    K, D = case.block_size, case.head_dim
     total = 0
     for n in seq_lens.tolist():
-        c = n - case.block_size
+        c = n - K
         lo = max(0, c - case.window_left + 1) if case.window_left > 0 else 0
-        total += case.num_kv_heads * (n - lo) * 2 * eb * case.head_dim
+        if block == "cache":
+            total += case.num_kv_heads * (n - lo) * 2 * eb * D
+        else:
+            total += case.num_kv_heads * ((c - lo) * 2 * eb * D + K * 2 * 2 * D)
+            if block == "append":
+                total += case.num_kv_heads * K * 2 * eb * D
     return total
 
 
@@ -115,7 +125,7 @@ def load_traffic(case_name: str, per_launch_bytes: int):
     return rec.get("hbm_bytes_per_launch")
 
 
-def run_case(case, steps, warmup, threads, graph=True, splits=0, waves=0):
+def run_case(case, steps, warmup, threads, graph=True, splits=0, waves=0, block="cache"):
     import numpy as np
     import torch
 
@@ -153,9 +163,17 @@ def run_case(case, steps, warmup, threads, graph=True, splits=0, waves=0):
     out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     fwd = ba.blockattn_windowed_forward if case.windowed else ba.blockattn_forward
+    blocks = None
+    if block != "cache":
+        blocks = synth.make_block(case, threads=threads)
+        kb, vb = bf(blocks[0]), bf(blocks[1])
 
     def step(i):
-        fwd(plan, q, ks[i % copies], vs[i % copies], pt, lens, ws, out, lse)
+        if blocks is None:
+            fwd(plan, q, ks[i % copies], vs[i % copies], pt, lens, ws, out, lse)
+        else:
+            ba.blockattn_forward_block(plan, q, kb, vb, ks[i % copies], vs[i % copies], pt, lens, ws, out, lse,
+                                       append=block == "append")
 
     for i in range(warmup):
         step(i)
@@ -211,7 +229,8 @@ def run_case(case, steps, warmup, threads, graph=True, splits=0, waves=0):
     info = plan.info()
     res = {
         "case": case.name,
-        "kv_bytes": kv_bytes(case, inp.seq_lens),
+        "kv_bytes": kv_bytes(case, inp.seq_lens, block),
+        "block": block,
         "step_ms": total_ms / steps,
         "wall_ms": wall * 1e3 / steps,
         "partial_ms": sum(kern_ms) / len(kern_ms),
@@ -226,7 +245,7 @@ def run_case(case, steps, warmup, threads, graph=True, splits=0, waves=0):
         "combine_launch": info["combine_launch"],
     }
     plan.destroy()
-    return res, inp, out
+    return res, inp, out, blocks
 
 
 COPY_ELEMS = 1 << 28  # float32 elements of the reference copy: 1 GiB read + 1 GiB written per launch
@@ -299,7 +318,7 @@ def pmc_summary(case_name, fetch_path, write_path):
     return out
 
 
-def cpu_baseline(case, inp, gpu_out, kv_total, budget_s):
+def cpu_baseline(case, inp, gpu_out, kv_total, budget_s, blocks=None):
     """Time the fp64 oracle on a bounded sample of (request, kv head) pairs of the same call."""
     import numpy as np
 
@@ -307,14 +326,15 @@ def cpu_baseline(case, inp, gpu_out, kv_total, budget_s):
 
     threads = oracle.default_threads()
     pairs_all = [(b, h) for b in range(case.batch) for h in range(case.num_kv_heads)]
+    kb, vb = blocks if blocks is not None else (None, None)
     t0 = time.perf_counter()
-    out, lse = oracle.attention_case(inp, pairs=pairs_all[:1], threads=threads)
+    out, lse = oracle.attention_case(inp, pairs=pairs_all[:1], threads=threads, k_block=kb, v_block=vb)
     t1 = time.perf_counter() - t0
     n = max(1, min(len(pairs_all), int(budget_s / max(t1, 1e-3))))
     sample = pairs_all[:n]
     if n > 1:
         t0 = time.perf_counter()
-        out, lse = oracle.attention_case(inp, pairs=sample, threads=threads)
+        out, lse = oracle.attention_case(inp, pairs=sample, threads=threads, k_block=kb, v_block=vb)
         t1 = time.perf_counter() - t0
     per_pair = t1 / len(sample)
     full_s = per_pair * len(pairs_all)
@@ -351,16 +371,20 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--splits", type=int, default=0, help="force the split count per (request, kv head)")
     ap.add_argument("--waves", type=int, default=0, help="force the tile-streaming waves per workgroup")
+    ap.add_argument("--block", choices=("cache", "dense", "append"), default="cache",
+                    help="where the block's keys and values come from: the cache (default), dense arrays, or "
+                         "dense arrays also appended into the cache in the same call")
     ap.add_argument("--copy-reference", action="store_true",
                     help="also time a plain 1 GiB elementwise copy (achievable HBM rate; PMC calibration kernel)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH", "WRITE"),
                     help="no GPU: read two rocprofv3 --pmc outputs (FETCH_SIZE, WRITE_SIZE) of a --copy-reference "
-                         "run of --case and write profiles/pmc_partial_<case>.json")
+                         "run of --case (and --block) and write profiles/pmc_partial_<case>[_<block>].json")
     args = ap.parse_args()
 
+    label = args.case if args.block == "cache" else f"{args.case}_{args.block}"
     if args.pmc_summary:
-        rec = pmc_summary(args.case, *args.pmc_summary)
-        with open(os.path.join(ROOT, "profiles", f"pmc_partial_{args.case}.json"), "w") as f:
+        rec = pmc_summary(label, *args.pmc_summary)
+        with open(os.path.join(ROOT, "profiles", f"pmc_partial_{label}.json"), "w") as f:
             json.dump(rec, f, indent=1)
             f.write("\n")
         print(json.dumps(rec))
@@ -378,8 +402,8 @@ def main():
     threads = min(16, len(os.sched_getaffinity(0)))
 
     case = find_case(args.case)
-    res, inp, out = run_case(case, args.steps, args.warmup, threads, graph=not args.eager, splits=args.splits,
-                             waves=args.waves)
+    res, inp, out, blocks = run_case(case, args.steps, args.warmup, threads, graph=not args.eager,
+                                     splits=args.splits, waves=args.waves, block=args.block)
     kvb = res["kv_bytes"]
     value = kvb / (res["step_ms"] * 1e-3) / 1e9
     achieved = kvb / (res["partial_ms"] * 1e-3) / 1e9
@@ -393,8 +417,8 @@ def main():
         for c in cases_for_config(case.cfg):
             if case.kv_dtype != "bf16":
                 c = fp8_variant(c, case.k_scale, case.v_scale)
-            r, _, _ = run_case(c, max(10, args.steps // 2), 3, threads, graph=not args.eager, splits=args.splits,
-                               waves=args.waves)
+            r, _, _, _ = run_case(c, max(10, args.steps // 2), 3, threads, graph=not args.eager,
+                                  splits=args.splits, waves=args.waves, block=args.block)
             r["gbs"] = r["kv_bytes"] / (r["step_ms"] * 1e-3) / 1e9
             r["frac"] = r["gbs"] / HBM_PEAK_GBS
             r["partial_gbs"] = r["kv_bytes"] / (r["partial_ms"] * 1e-3) / 1e9
@@ -405,7 +429,7 @@ def main():
             torch.cuda.empty_cache()
 
     copy_ref = copy_reference() if args.copy_reference else None
-    traffic = load_traffic(case.name, kvb)
+    traffic = load_traffic(label, kvb)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -425,7 +449,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{case.name}: draft-block attention, {case.num_q_heads}q/{case.num_kv_heads}kv heads, "
                                f"head_dim {case.head_dim}, K={case.block_size}, page {case.page_size}, "
-                               f"{'windowed W=%d' % case.window_left if case.windowed else 'unwindowed'}",
+                               f"{'windowed W=%d' % case.window_left if case.windowed else 'unwindowed'}"
+                               + {"cache": "", "dense": ", block K/V from dense arrays",
+                                  "append": ", block K/V from dense arrays and appended to the cache"}[args.block],
+                   "block_kv": args.block,
                    "batch": case.batch, "context": case.context, "kv_dtype": case.kv_dtype,
                    "k_scale": case.k_scale, "v_scale": case.v_scale, "kv_bytes_per_call": kvb,
                    "pool_copies_rotated": res["copies"], "hip_graph": res["graph"], "units": res["units"],
@@ -442,7 +469,7 @@ def main():
     if sweep is not None:
         line["sweep"] = [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()} for r in sweep]
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(case, inp, out, kvb, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(case, inp, out, kvb, args.cpu_seconds, blocks)
     print(json.dumps(line), flush=True)
 
 

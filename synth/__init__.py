@@ -51,6 +51,8 @@ def _load():
     lib.synth_bf16_from_double.restype = ctypes.c_uint16
     lib.synth_fill_q.argtypes = [u64, i64, ptr, i32]
     lib.synth_fill_q.restype = None
+    lib.synth_fill_normal.argtypes = [u64, i32, i64, ptr, i32]
+    lib.synth_fill_normal.restype = None
     lib.synth_context_lengths.argtypes = [u64, i32, i32, i32, ptr]
     lib.synth_context_lengths.restype = None
     lib.synth_pages_needed.argtypes = [i32, ptr, i32]
@@ -130,6 +132,18 @@ def make_q(case: Case, threads: int | None = None) -> np.ndarray:
     q = np.empty((case.batch, case.block_size, case.num_q_heads, case.head_dim), dtype=np.uint16)
     lib.synth_fill_q(case.seed, q.size, _p(q), threads or default_threads())
     return q
+
+
+def make_block(case: Case, threads: int | None = None):
+    """Dense block keys and values, bf16 bits [B, K, Hkv, D] each (N(0, 1) draws, unscaled)."""
+    lib = _load()
+    shape = (case.batch, case.block_size, case.num_kv_heads, case.head_dim)
+    out = []
+    for tensor_id in (7, 8):
+        a = np.empty(shape, dtype=np.uint16)
+        lib.synth_fill_normal(case.seed, tensor_id, a.size, _p(a), threads or default_threads())
+        out.append(a)
+    return out[0], out[1]
 
 
 def make_pool(case: Case, tensor_id: int, seq_lens: np.ndarray, page_table: np.ndarray, num_pages: int,

@@ -120,8 +120,12 @@ static int clamp_threads(int threads) {
 }
 
 void synth_fill_q(uint64_t seed, int64_t count, uint16_t* q, int threads) {
+    synth_fill_normal(seed, SYNTH_TENSOR_Q, count, q, threads);
+}
+
+void synth_fill_normal(uint64_t seed, int tensor_id, int64_t count, uint16_t* q, int threads) {
     threads = clamp_threads(threads);
-    const uint64_t key = synth_key(seed, SYNTH_TENSOR_Q);
+    const uint64_t key = synth_key(seed, (uint64_t)tensor_id);
     pthread_t tid[256];
     q_job jobs[256];
     for (int t = 0; t < threads; ++t) {

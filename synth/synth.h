@@ -14,7 +14,9 @@ enum {
     SYNTH_TENSOR_V = 3,
     SYNTH_TENSOR_PERM = 4,
     SYNTH_TENSOR_CTX = 5,
-    SYNTH_TENSOR_OUTLIER = 6
+    SYNTH_TENSOR_OUTLIER = 6,
+    SYNTH_TENSOR_K_BLOCK = 7,  /* dense block keys [B, K, Hkv, D] */
+    SYNTH_TENSOR_V_BLOCK = 8
 };
 
 uint64_t synth_key(uint64_t seed, uint64_t tensor);
@@ -25,6 +27,8 @@ uint16_t synth_bf16_from_double(double x);
 
 /* q[count] bf16 N(0,1), element n drawn from stream (seed, q). */
 void synth_fill_q(uint64_t seed, int64_t count, uint16_t* q, int threads);
+/* count N(0, 1) draws of stream (seed, tensor_id), rounded to bf16 (q uses SYNTH_TENSOR_Q) */
+void synth_fill_normal(uint64_t seed, int tensor_id, int64_t count, uint16_t* dst, int threads);
 
 /* out[b] uniform integer in [lo, hi] from stream (seed, context lengths). */
 void synth_context_lengths(uint64_t seed, int batch, int lo, int hi, int32_t* out);

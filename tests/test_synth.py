@@ -56,6 +56,26 @@ def test_normal_moments_and_outliers():
     assert not np.array_equal(inp.q.ravel()[:64], inp.k_pool.ravel()[:64])
 
 
+def test_dense_block_draws():
+    case = Case("t", 92, 1, batch=4, block_size=7, num_q_heads=16, num_kv_heads=2, head_dim=128, page_size=64,
+                context=100)
+    kb, vb = synth.make_block(case)
+    assert kb.shape == vb.shape == (4, 7, 2, 128) and kb.dtype == np.uint16
+    kb2, vb2 = synth.make_block(case)
+    assert np.array_equal(kb, kb2) and np.array_equal(vb, vb2)
+    q = synth.make_q(case)
+    for a in (kb, vb):
+        x = synth.bf16_bits_to_float(a).astype(np.float64)
+        assert abs(x.mean()) < 0.05 and abs(x.std() - 1.0) < 0.05
+    # three different streams
+    assert not np.array_equal(kb.ravel()[:64], vb.ravel()[:64])
+    assert not np.array_equal(kb.ravel()[:64], q.ravel()[:64])
+    # the query stream is the generic normal fill of tensor 1
+    q2 = np.empty_like(q)
+    synth._load().synth_fill_normal(case.seed, 1, q2.size, q2.ctypes.data, 3)
+    assert np.array_equal(q, q2)
+
+
 def test_bf16_rounding_is_nearest_even():
     lib = synth._load()
     assert lib.synth_bf16_from_double(1.0) == 0x3F80
