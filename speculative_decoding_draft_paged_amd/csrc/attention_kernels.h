@@ -205,6 +205,9 @@ struct WaveRows {
     bool on[NBW];
     f32x4_t acc[NBW][DB];
     float m[NBW], l[NBW];
+    float neg_m[NBW];  // -m, or 0 while m = -inf
+    float gate[NBW];   // exponent arguments above this need the slow path: -inf before a row's first key
+                       // (so any key sets m), the rescale slack after
     int lo_max, hi_min;
     int hi_cap;  // keys at or past this come from elsewhere (the dense block) and are masked here
 
@@ -231,6 +234,8 @@ struct WaveRows {
             row_hi[n] = WINDOWED ? min(u.N - 1, p + right) : u.N - 1;
             m[n] = kNegInf;
             l[n] = 0.f;
+            neg_m[n] = 0.f;
+            gate[n] = kNegInf;
 #pragma unroll
             for (int db = 0; db < DB; ++db) acc[n][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
@@ -287,29 +292,41 @@ struct WaveRows {
                         if (tok < row_lo[n] || tok > row_hi[n] || tok >= hi_cap) x[mb * 4 + j] = kNegInf;
                     }
             }
-            float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-            mx = quad_max(mx);
-            const float mxs = mx * scale;  // scale > 0, so the maximum commutes with it
-            if (mxs > m[n] + kRescaleSlack) {
-                const float alpha = fast_exp2(m[n] - mxs);
-                l[n] *= alpha;
+            // Exponent arguments against the current reference. They are arithmetic
+            // results, so their maximum needs no operand canonicalisation. The row's
+            // four-lane maximum is needed only when an argument passes the gate; a row's
+            // maximum is at least each of its lanes' maxima, so when no lane of the wave
+            // passes (the common case after a row's first tile) no row needs a rescale.
+            float y[8];
 #pragma unroll
-                for (int db = 0; db < DB; ++db) acc[n][db] *= alpha;
-                m[n] = mxs;
+            for (int k = 0; k < 8; ++k) y[k] = fmaf(x[k], scale, neg_m[n]);
+            const float ymax = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])), fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
+            if (__builtin_amdgcn_ballot_w64(ymax > gate[n]) != 0) {
+                const float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+                const float mxs = quad_max(mx) * scale;  // scale > 0, so the maximum commutes with it
+                if (mxs > m[n] + kRescaleSlack) {
+                    const float alpha = fast_exp2(m[n] - mxs);
+                    l[n] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) acc[n][db] *= alpha;
+                    m[n] = mxs;
+                    neg_m[n] = -mxs;
+                    gate[n] = kRescaleSlack;
+                }
+#pragma unroll
+                for (int k = 0; k < 8; ++k) y[k] = fmaf(x[k], scale, neg_m[n]);
             }
-            const float neg_m = m[n] == kNegInf ? 0.f : -m[n];
             bf16x8_t pb;
-            float psum = 0.f;
+            float p[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const float p = fast_exp2(fmaf(x[k], scale, neg_m));
-                psum += p;
+                p[k] = fast_exp2(y[k]);
                 if constexpr (PMUL)
-                    pb[k] = (__bf16)(p * pmul);
+                    pb[k] = (__bf16)(p[k] * pmul);
                 else
-                    pb[k] = (__bf16)p;
+                    pb[k] = (__bf16)p[k];
             }
-            l[n] += psum;
+            l[n] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
 #pragma unroll
             for (int db = 0; db < DB; ++db)
                 acc[n][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pb, acc[n][db], 0, 0, 0);
@@ -852,50 +869,63 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const KernelArgs a) {
     constexpr int DL = D / 4;     // threads per split row, 4 floats each
-    constexpr int SL = 256 / DL;  // splits reduced in parallel
+    constexpr int SL = 256 / DL;  // split streams reduced in parallel
     __shared__ float red_acc[SL][D];
     __shared__ float red_l[SL];
-    __shared__ float red_m[4];
+    __shared__ float red_m[SL];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x;
     const int row = blockIdx.x;
     const int pair = row / a.R, r = row - (row / a.R) * a.R;
     const int b = pair / a.Hkv, hk = pair - (pair / a.Hkv) * a.Hkv;
-    const int u0 = a.pair_table[2 * pair], S = a.pair_table[2 * pair + 1];
+    int u0, S;
+    if (a.uniform_splits > 0) {  // units are laid out pair by pair: no table load
+        S = a.uniform_splits;
+        u0 = pair * S;
+    } else {
+        u0 = a.pair_table[2 * pair];
+        S = a.pair_table[2 * pair + 1];
+    }
     if (S <= 1) return;  // a single split wrote its output itself
     const int i = r / a.g, l = r - (r / a.g) * a.g, h = hk * a.g + l;
     const size_t orow = (size_t)(b * a.K + i) * a.Hq + h;
 
-    float mloc = kNegInf;
-#pragma unroll 2
-    for (int s = tid; s < S; s += 256) mloc = fmaxf(mloc, a.part_m[(size_t)(u0 + s) * a.R + r]);
-    for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
-    if (lane == 0) red_m[wave] = mloc;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
-
+    // One pass: each thread folds its splits into a running (m, l, acc) state, so every
+    // load is independent of the others. A state with m = -inf (no keys) weighs 0, and
+    // 0 * NaN still carries a NaN sum through.
     const int d4 = tid % DL, sl = tid / DL;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    float lsum = 0.f;
-    // A split with no keys (m = -inf) weighs 0; 0 * NaN still carries a NaN sum through.
+    float m = kNegInf, lsum = 0.f;
 #pragma unroll 4
     for (int s = sl; s < S; s += SL) {
         const size_t pr = (size_t)(u0 + s) * a.R + r;
         const float ms = a.part_m[pr];
-        const float wgt = ms == kNegInf ? 0.f : fast_exp2(ms - M);
-        acc += wgt * *(const f32x4_t*)(a.part_acc + pr * D + 4 * d4);
-        lsum += wgt * a.part_l[pr];
+        const float ls = a.part_l[pr];
+        const f32x4_t as = *(const f32x4_t*)(a.part_acc + pr * D + 4 * d4);
+        const float mn = fmaxf(m, ms);
+        const float wa = m == kNegInf ? 0.f : fast_exp2(m - mn);
+        const float wb = ms == kNegInf ? 0.f : fast_exp2(ms - mn);
+        acc = acc * wa + as * wb;
+        lsum = lsum * wa + ls * wb;
+        m = mn;
     }
     *(f32x4_t*)&red_acc[sl][4 * d4] = acc;
-    if (d4 == 0) red_l[sl] = lsum;
-    __syncthreads();
-    float L = 0.f;
-    for (int k = 0; k < SL; ++k) L += red_l[k];
-    if (tid < D) {
-        float o = 0.f;
-        for (int k = 0; k < SL; ++k) o += red_acc[k][tid];
-        a.out[orow * D + tid] = f32_to_bf16_rne(L == 0.f ? 0.f : o / L);
+    if (d4 == 0) {
+        red_l[sl] = lsum;
+        red_m[sl] = m;
     }
+    __syncthreads();
+    float M = kNegInf;
+#pragma unroll
+    for (int k = 0; k < SL; ++k) M = fmaxf(M, red_m[k]);
+    float L = 0.f, o = 0.f;
+#pragma unroll
+    for (int k = 0; k < SL; ++k) {
+        const float wk = red_m[k] == kNegInf ? 0.f : fast_exp2(red_m[k] - M);
+        L += wk * red_l[k];
+        if (tid < D) o += wk * red_acc[k][tid];
+    }
+    if (tid < D) a.out[orow * D + tid] = f32_to_bf16_rne(L == 0.f ? 0.f : o / L);
     if (tid == 0 && a.lse) a.lse[orow] = L == 0.f ? kNegInf : M + log2f(L);
 }
 
