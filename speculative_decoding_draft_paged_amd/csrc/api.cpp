@@ -157,11 +157,13 @@ KernelShape choose_shape(int D, int NB, int R, int waves_override) {
     s.shared = s.row_waves > 1;
     s.token_groups = s.shared ? 1 : std::max(1, std::min(4, max_waves / s.row_waves));
     if (s.shared && D == 128) {
-        // One row block per wave and up to 8 waves (two per SIMD, each within 256
-        // registers) from five row blocks on, so two waves per SIMD hide each other's
-        // latency; fewer rows keep two blocks per wave. waves_override picks the
-        // waves per workgroup: rows per wave = ceil(blocks / waves), 1 or 2.
-        int wv = NB >= 5 ? NB : s.row_waves;
+        // One row block per wave, up to 8 waves (two per SIMD, each within 256
+        // registers), so two waves per SIMD hide each other's latency. Measured on the
+        // windowed mixed batch: at three row blocks, three waves of one block beat two
+        // waves of two (121 against 138 us per call); at seven, seven waves beat four
+        // (151 against 197 us). waves_override picks the waves per workgroup: rows per
+        // wave = ceil(blocks / waves), 1 or 2.
+        int wv = NB;
         if (waves_override > 0) wv = std::max((NB + 1) / 2, std::min(waves_override, NB));
         s.nbw = (NB + wv - 1) / wv;
         s.row_waves = (NB + s.nbw - 1) / s.nbw;

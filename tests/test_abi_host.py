@@ -83,7 +83,9 @@ def test_tile_kernel_choice():
     w = dict(head_dim=128, page_size=64, num_q_heads=16, num_kv_heads=1, window_left=4096)
     info = plan_info(params(**w, block_size=5), [8197, 8197])  # R = 80: one row block per wave
     assert info["shared_tiles"] == 1 and info["row_waves"] == 5 and info["token_groups"] == 1
-    info = plan_info(params(**w, block_size=3), [8195, 8195])  # R = 48: two blocks per wave
+    info = plan_info(params(**w, block_size=3), [8195, 8195])  # R = 48: one block per wave as well
+    assert info["shared_tiles"] == 1 and info["row_waves"] == 3
+    info = plan_info(params(**w, block_size=3, waves_override=2), [8195, 8195])  # two blocks per wave
     assert info["shared_tiles"] == 1 and info["row_waves"] == 2
     assert plan_info(params(**w, block_size=1), [8193, 8193])["shared_tiles"] == 0  # R = 16
 

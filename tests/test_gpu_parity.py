@@ -107,7 +107,7 @@ def test_split_invariance_shared_tiles(splits):
     assert np.abs(out - base).max() <= 4 * H.ulp_bf16(float(np.abs(base).max()))
 
 
-@pytest.mark.parametrize("K,waves,row_waves", [(7, 4, 4), (5, 3, 3), (3, 3, 3), (7, 8, 7)])
+@pytest.mark.parametrize("K,waves,row_waves", [(7, 4, 4), (5, 3, 3), (3, 3, 3), (3, 2, 2), (3, 0, 3), (7, 8, 7)])
 def test_rows_per_wave_variants(K, waves, row_waves):
     """Every row-blocks-per-wave choice of the shared-tile kernel at D = 128 meets the bar."""
     c = case(37 + K, batch=2, K=K, hq=16, hkv=1, D=128, P=64, ctx=2500, wl=1000, wr=-1)
