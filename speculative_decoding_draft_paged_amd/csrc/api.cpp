@@ -155,7 +155,10 @@ KernelShape choose_shape(int D, int NB, int R, int waves_override) {
     const int max_waves = D == 64 ? kMaxWaves : 4;
     // More than one row-wave: the workgroup shares each tile through LDS, one token stream.
     s.shared = s.row_waves > 1;
-    s.token_groups = s.shared ? 1 : std::max(1, std::min(4, max_waves / s.row_waves));
+    // Token groups: as many as the workgroup allows. At D = 64 eight groups beat four by
+    // 0.5-4 % over the unwindowed batches measured (one 8-wave workgroup per CU instead
+    // of two of 4 waves) and tie on the wider ones.
+    s.token_groups = s.shared ? 1 : std::max(1, max_waves / s.row_waves);
     if (s.shared && D == 128) {
         // One row block per wave, up to 8 waves (two per SIMD, each within 256
         // registers), so two waves per SIMD hide each other's latency. Measured on the

@@ -54,7 +54,7 @@ def test_host_only_plan_and_info():
 def test_split_heuristic_fills_the_gpu_and_bounds_partials():
     # one request, 128K keys, 2 kv heads: many splits; 32 requests x 16 heads: one split each
     small = plan_info(params(batch=1), [131079])
-    assert small["units"] >= 256
+    assert small["units"] >= 240  # about one unit per CU (4097 tiles of each head in 125 splits)
     big = plan_info(params(batch=32, num_q_heads=64, num_kv_heads=16), [131079] * 32)
     assert big["max_splits"] == 1 and big["units"] == 512
     # every token group gets at least two tiles
