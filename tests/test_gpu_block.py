@@ -86,6 +86,9 @@ CASES = [
     # scales that are not powers of two (block probabilities rounded after the 1 / v_scale product)
     (10, dict(fp8=True, batch=2, K=7, hq=8, hkv=2, D=64, P=32, ctx=600, ks=0.3, vs=-0.7)),
     (11, dict(batch=2, K=5, hq=32, hkv=2, D=128, P=64, ctx=1500, ks=0.37, vs=1.9)),    # bf16 cache with scales
+    (12, dict(batch=2, K=16, hq=2, hkv=1, D=64, P=128, ctx=700, wl=300, wr=-1)),      # largest block, 128-token pages
+    (13, dict(batch=3, K=16, hq=8, hkv=1, D=128, P=16, ctx_range=(0, 400), wl=50, wr=3)),  # R = 128, 8 row-waves
+    (14, dict(fp8=True, batch=2, K=2, hq=48, hkv=2, D=64, P=32, ctx=333, wl=40, wr=0)),   # shared tiles at D = 64, causal
 ]
 
 
@@ -128,7 +131,7 @@ def expected_append(inp, kb, vb):
     return k, v
 
 
-APPEND = [CASES[i] for i in (0, 2, 4, 5, 7, 8)]
+APPEND = [CASES[i] for i in (0, 2, 4, 5, 7, 8, 9, 10, 11)]
 
 
 @pytest.mark.parametrize("idx,kw", APPEND, ids=[f"bk{i}" for i, _ in APPEND])
