@@ -60,7 +60,7 @@ extern "C" {
 typedef enum blockattn_status {
     BLOCKATTN_OK = 0,
     BLOCKATTN_ERR_INVALID_ARGUMENT = 1,  /* a shape, length, pointer or window out of range */
-    BLOCKATTN_ERR_UNSUPPORTED = 2,       /* a valid shape this build has no kernel for (D, P, R) */
+    BLOCKATTN_ERR_UNSUPPORTED = 2,       /* a valid shape the library has no kernel for (D, P, R) */
     BLOCKATTN_ERR_WORKSPACE_TOO_SMALL = 3,
     BLOCKATTN_ERR_PLAN_MISMATCH = 4,     /* forward kind or workspace differs from the plan's */
     BLOCKATTN_ERR_HIP = 5                /* the HIP runtime reported an error */
