@@ -72,7 +72,7 @@ typedef struct blockattn_params {
     int32_t num_q_heads;       /* Hq, a multiple of Hkv */
     int32_t num_kv_heads;      /* Hkv >= 1 */
     int32_t head_dim;          /* D: 64 or 128 */
-    int32_t page_size;         /* P tokens per page: 16, 32, 64 or 128 */
+    int32_t page_size;         /* P tokens per page: 16, 32, 64, 128 or 256 */
     int32_t page_table_stride; /* int32 entries per page-table row, >= ceil(N_b / P) */
     int32_t num_pages;         /* pages in each pool; page ids must lie in [0, num_pages) */
     int32_t window_left;       /* -1: unwindowed form; W >= 1: windowed form, causal window of W keys */

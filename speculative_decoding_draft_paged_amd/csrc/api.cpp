@@ -80,8 +80,10 @@ int validate(const blockattn_params* p, const int32_t* lens) {
         return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "num_q_heads must be a positive multiple of num_kv_heads >= 1");
     if (p->head_dim != 64 && p->head_dim != 128)
         return fail(BLOCKATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (the gfx950 kernels are built for those)");
-    if (p->page_size != 16 && p->page_size != 32 && p->page_size != 64 && p->page_size != 128)
-        return fail(BLOCKATTN_ERR_UNSUPPORTED, "page_size must be 16, 32, 64 or 128 tokens");
+    // Any power of two from 16 (half a 32-token tile, so a half never spans two pages) to
+    // 256 (a target pool's page size when the draft context lives in the target's pool).
+    if (p->page_size < 16 || p->page_size > 256 || (p->page_size & (p->page_size - 1)) != 0)
+        return fail(BLOCKATTN_ERR_UNSUPPORTED, "page_size must be 16, 32, 64, 128 or 256 tokens");
     const int g = p->num_q_heads / p->num_kv_heads;
     const long R = (long)p->block_size * g;
     if (R > 16L * kMaxRowBlocks)

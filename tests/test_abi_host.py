@@ -124,6 +124,8 @@ def test_workspace_size_grows_with_batch(B):
     (dict(k_scale=float("inf")), [100, 100], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "k_scale"),
     (dict(v_scale=float("nan")), [100, 100], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "v_scale"),
     (dict(page_size=48), [100, 100], ba.BLOCKATTN_ERR_UNSUPPORTED, "page_size"),
+    (dict(page_size=8), [100, 100], ba.BLOCKATTN_ERR_UNSUPPORTED, "page_size"),
+    (dict(page_size=512), [100, 100], ba.BLOCKATTN_ERR_UNSUPPORTED, "page_size"),
     (dict(num_q_heads=7), [100, 100], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "num_q_heads"),
     (dict(block_size=17), [100, 100], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "block_size"),
     (dict(num_q_heads=40, num_kv_heads=1, block_size=4), [100, 100], ba.BLOCKATTN_ERR_UNSUPPORTED, "128"),

@@ -140,3 +140,10 @@ def test_fp8_config_case(name):
         sel[b, :, h * g:(h + 1) * g] = True
     res = H.compare(out, lse, ref_out, ref_lse, sel=sel, label=name)
     print(f"[{name}] {res} units={info['units']}", flush=True)
+
+
+@pytest.mark.parametrize("idx,kw", [(70, dict(batch=2, K=7, hq=8, hkv=2, D=64, P=256, ctx_range=(0, 1200))),
+                                     (71, dict(batch=2, K=7, hq=16, hkv=1, D=128, P=256, ctx=1800, wl=500, wr=-1))],
+                         ids=["p256_stream", "p256_shared"])
+def test_fp8_pages_of_256_tokens(idx, kw):
+    check_full(case8(idx, **kw), f"fp8 p256_{idx}")

@@ -185,3 +185,18 @@ def test_workspace_canary_and_no_nan_leak():
     assert (inp.k_pool[-1] == synth.BF16_NAN).all()
     out, lse, _ = H.run(H.upload(inp), canary=True)
     assert np.isfinite(out).all() and np.isfinite(lse).all()
+
+
+# 256-token pages: the size of a target model's pool when the draft context lives in it.
+PAGES_256 = [
+    (60, dict(batch=3, K=7, hq=8, hkv=2, D=64, P=256, ctx_range=(0, 1500))),                 # streaming
+    (61, dict(batch=2, K=7, hq=16, hkv=1, D=128, P=256, ctx=2000, wl=300, wr=-1)),          # shared tiles
+    (62, dict(batch=2, K=3, hq=16, hkv=1, D=128, P=256, ctx_range=(200, 900), wl=4096, wr=1)),
+    (63, dict(batch=1, K=16, hq=2, hkv=1, D=64, P=256, ctx=255)),                          # block across a page edge
+]
+
+
+@pytest.mark.parametrize("idx,kw", PAGES_256, ids=[f"p256_{i}" for i, _ in PAGES_256])
+def test_pages_of_256_tokens(idx, kw):
+    check_full(case(idx, **kw), f"p256_{idx}")
+    check_full(case(idx, **kw), f"p256_{idx} splits=3", splits=3)
