@@ -46,6 +46,7 @@
 
 #include <math.h>
 
+#include <atomic>
 #include <type_traits>
 
 namespace blockattn {
@@ -929,13 +930,31 @@ __global__ __launch_bounds__(256) void combine_kernel(const KernelArgs a) {
     if (tid == 0 && a.lse) a.lse[orow] = L == 0.f ? kNegInf : M + log2f(L);
 }
 
+// Dynamic LDS above 64 KiB needs the kernel's limit raised, once per device (the
+// attribute applies to the current device). Devices past the table are raised on
+// every launch.
+constexpr int kLdsGrantDevices = 64;
+struct LdsGrant {
+    std::atomic<size_t> bytes[kLdsGrantDevices];  // static storage: starts at zero
+};
+
 template <typename F>
 hipError_t launch_with_lds(F fn, int units, int threads, size_t lds, const KernelArgs& args, hipStream_t stream,
-                           size_t* granted) {
-    if (lds > 65536 && lds > *granted) {
-        hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                           LdsGrant& grant) {
+    if (lds > 65536) {
+        int dev = -1;
+        hipError_t e = hipGetDevice(&dev);
         if (e != hipSuccess) return e;
-        *granted = lds;
+        const bool tracked = dev >= 0 && dev < kLdsGrantDevices;
+        if (!tracked || grant.bytes[dev].load(std::memory_order_relaxed) < lds) {
+            e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            if (tracked) {
+                size_t cur = grant.bytes[dev].load(std::memory_order_relaxed);
+                while (cur < lds && !grant.bytes[dev].compare_exchange_weak(cur, lds, std::memory_order_relaxed)) {
+                }
+            }
+        }
     }
     hipLaunchKernelGGL(fn, dim3(units), dim3(threads), lds, stream, args);
     return hipGetLastError();
@@ -943,10 +962,10 @@ hipError_t launch_with_lds(F fn, int units, int threads, size_t lds, const Kerne
 
 template <int D, int NBW, bool W, bool ALL_ON, bool FP8>
 hipError_t launch_stream(const KernelShape& s, int units, const KernelArgs& args, hipStream_t stream) {
-    static size_t granted = 0;
+    static LdsGrant grant;
     constexpr int MAXT = D == 64 ? 512 : 256;  // D = 128 keeps workgroups small so a wave may use 512 registers
     return launch_with_lds(stream_kernel<D, NBW, W, ALL_ON, MAXT, FP8>, units, 64 * s.row_waves * s.token_groups,
-                           s.lds_bytes, args, stream, &granted);
+                           s.lds_bytes, args, stream, grant);
 }
 
 // Tiles in flight per lane: about 96 registers of staged loads for a wave alone on
@@ -959,9 +978,9 @@ constexpr int shared_depth(int D, int NBW, int WR, bool FP8) {
 
 template <int D, int NBW, int WR, bool W, bool ALL_ON, bool FP8>
 hipError_t launch_shared(const KernelShape& s, int units, const KernelArgs& args, hipStream_t stream) {
-    static size_t granted = 0;
+    static LdsGrant grant;
     return launch_with_lds(shared_kernel<D, NBW, W, ALL_ON, WR, shared_depth(D, NBW, WR, FP8), FP8>, units, 64 * WR,
-                           s.lds_bytes, args, stream, &granted);
+                           s.lds_bytes, args, stream, grant);
 }
 
 template <bool W, bool FP8>
