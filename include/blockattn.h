@@ -3,8 +3,8 @@
  *
  * A speculative-decoding drafter proposes a block of K draft tokens per
  * request. Each of the K block queries (times the GQA group, so R = K * Hq/Hkv
- * query rows per KV head) attends to the request's paged context plus the K
- * block keys, which are already appended to the cache.
+ * query rows per KV head, any number) attends to the request's paged context
+ * plus the K block keys, which are already appended to the cache.
  *
  *  - blockattn_forward: the non-causal unwindowed form. Every block query of a
  *    request sees the same N_b = seq_lens[b] keys (TensorRT-LLM PR #20374,
@@ -111,6 +111,9 @@ typedef struct blockattn_plan_info {
                                   more than one split); 0: every split wrote its output directly */
     int32_t shared_tiles;      /* 1: each workgroup loads a tile once into LDS for all its row waves
                                   (R > 32); 0: each wave streams its own tiles */
+    int32_t row_groups;        /* work units per (request, kv head, split): 1 up to 128 query rows per
+                                  kv head; above that the rows are split into this many groups of at
+                                  most 128, each reading the kv head's keys */
     size_t workspace_bytes;    /* bytes the plan needs */
 } blockattn_plan_info_t;
 

@@ -75,6 +75,7 @@ class blockattn_plan_info_t(ctypes.Structure):
         ("uploaded", ctypes.c_int32),
         ("combine_launch", ctypes.c_int32),
         ("shared_tiles", ctypes.c_int32),
+        ("row_groups", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 

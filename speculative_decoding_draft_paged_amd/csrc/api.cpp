@@ -53,7 +53,8 @@ struct Layout {
 struct blockattn_plan_s {
     blockattn_params prm{};
     int kind = 0;
-    int g = 1, R = 1, NB = 1;
+    int g = 1, R = 1, NB = 1;  // R: query rows per work unit (NB 16-row blocks)
+    int R_all = 1, G = 1;      // query rows per kv head, split into G row groups of R
     KernelShape shape{};
     bool merge_active = false;
     int units = 0, max_splits = 0;
@@ -85,10 +86,7 @@ int validate(const blockattn_params* p, const int32_t* lens) {
     if (p->page_size < 16 || p->page_size > 256 || (p->page_size & (p->page_size - 1)) != 0)
         return fail(BLOCKATTN_ERR_UNSUPPORTED, "page_size must be 16, 32, 64, 128 or 256 tokens");
     const int g = p->num_q_heads / p->num_kv_heads;
-    const long R = (long)p->block_size * g;
-    if (R > 16L * kMaxRowBlocks)
-        return fail(BLOCKATTN_ERR_UNSUPPORTED,
-                    "block_size * (num_q_heads / num_kv_heads) must be <= 128 query rows per kv head");
+    (void)g;  // any row count: more than 128 rows per kv head run as several row groups
     if (p->page_table_stride < 1) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "page_table_stride must be >= 1");
     if (p->num_pages < 1) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "num_pages must be >= 1");
     if ((int64_t)p->num_pages * p->num_kv_heads > INT32_MAX)
@@ -191,13 +189,18 @@ int build_plan(const blockattn_params* p, const int32_t* lens, blockattn_plan_s*
     pl->prm = *p;
     pl->kind = p->window_left == -1 ? 0 : 1;
     pl->g = p->num_q_heads / p->num_kv_heads;
-    pl->R = p->block_size * pl->g;
-    pl->NB = (pl->R + 15) / 16;
+    // More than 128 query rows per kv head: G row groups of equal 16-row blocks, each its
+    // own work unit that reads the kv head's keys again.
+    pl->R_all = p->block_size * pl->g;
+    const int blocks_all = (pl->R_all + 15) / 16;
+    pl->G = (blocks_all + kMaxRowBlocks - 1) / kMaxRowBlocks;
+    pl->NB = (blocks_all + pl->G - 1) / pl->G;
+    pl->R = pl->G == 1 ? pl->R_all : 16 * pl->NB;
     pl->shape = choose_shape(p->head_dim, pl->NB, pl->R, p->waves_override);
     pl->shape.fp8 = p->kv_dtype == BLOCKATTN_KV_FP8_E4M3;
     pl->merge_active = pl->kind == 1 && p->block_size > 1 && p->window_right != 0;
 
-    const int B = p->batch, H = p->num_kv_heads;
+    const int B = p->batch, H = p->num_kv_heads * pl->G;  // (kv head, row group) pairs per request
     std::vector<int> nt(B);
     long total = 0;
     for (int b = 0; b < B; ++b) {
@@ -318,6 +321,8 @@ int run_forward(blockattn_plan_t plan, const void* q, const void* k, const void*
     ka.Hkv = p.num_kv_heads;
     ka.g = plan->g;
     ka.R = plan->R;
+    ka.R_all = plan->R_all;
+    ka.row_groups = plan->G;
     ka.P = p.page_size;
     ka.p_shift = __builtin_ctz((unsigned)p.page_size);
     ka.stride = p.page_table_stride;
@@ -339,7 +344,7 @@ int run_forward(blockattn_plan_t plan, const void* q, const void* k, const void*
     if (e == hipSuccess && plan->prof_after) e = hipEventRecord(plan->prof_after, st);
     if (e != hipSuccess) return fail(BLOCKATTN_ERR_HIP, std::string("attention kernel launch: ") + hipGetErrorString(e));
     if (plan->max_splits > 1) {
-        const int rows = p.batch * p.num_kv_heads * plan->R;
+        const int rows = p.batch * p.num_kv_heads * plan->R_all;
         e = launch_combine(p.head_dim, rows, ka, st);
         if (e != hipSuccess)
             return fail(BLOCKATTN_ERR_HIP, std::string("combine kernel launch: ") + hipGetErrorString(e));
@@ -453,6 +458,7 @@ int blockattn_plan_info(blockattn_plan_t plan, blockattn_plan_info_t* info) {
     info->uploaded = plan->uploaded ? 1 : 0;
     info->combine_launch = plan->max_splits > 1 ? 1 : 0;
     info->shared_tiles = plan->shape.shared ? 1 : 0;
+    info->row_groups = plan->G;
     info->workspace_bytes = plan->lay.total;
     return BLOCKATTN_OK;
 }

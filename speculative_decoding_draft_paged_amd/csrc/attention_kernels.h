@@ -166,16 +166,17 @@ __device__ __forceinline__ float quad_sum(float x) {
 // N keys, the last K of them the block (p = C + i); NC of them are read from the
 // cache (N, or C when the block comes from dense arrays); tiles [ulo, uhi).
 struct Unit {
-    int b, hk, s, S, N, C, NC, ulo, uhi;
+    int b, hk, rg, s, S, N, C, NC, ulo, uhi;  // rg: row group (rows rg * R .. of the kv head)
 };
 
 template <bool WINDOWED>
 __device__ __forceinline__ Unit decode_unit(const KernelArgs& a) {
     WorkItem wi;
-    if (a.uniform_splits > 0) {  // every (request, kv head) has the same split count: no work-list load
+    const int hv_count = a.Hkv * a.row_groups;  // (kv head, row group) pairs per request
+    if (a.uniform_splits > 0) {  // every pair has the same split count: no work-list load
         const int pair = blockIdx.x / a.uniform_splits;
-        wi.b = pair / a.Hkv;
-        wi.hk = pair - wi.b * a.Hkv;
+        wi.b = pair / hv_count;
+        wi.hk = pair - wi.b * hv_count;
         wi.s = blockIdx.x - pair * a.uniform_splits;
         wi.S = a.uniform_splits;
     } else {
@@ -183,7 +184,8 @@ __device__ __forceinline__ Unit decode_unit(const KernelArgs& a) {
     }
     Unit u;
     u.b = wi.b;
-    u.hk = wi.hk;
+    u.hk = wi.hk / a.row_groups;
+    u.rg = wi.hk - u.hk * a.row_groups;
     u.s = wi.s;
     u.S = wi.S;
     u.N = clampi(a.seq_lens[wi.b], a.K, a.stride * a.P);
@@ -219,9 +221,10 @@ struct WaveRows {
 #pragma unroll
         for (int n = 0; n < NBW; ++n) {
             const int nb = first_block + n;
-            const int r = nb * 16 + r16;
-            on[n] = nb * 16 < a.R;
-            const bool live = r < a.R;
+            const int r0 = u.rg * a.R + nb * 16;  // first row of the block in the kv head's R_all rows
+            const int r = r0 + r16;
+            on[n] = nb * 16 < a.R && r0 < a.R_all;
+            const bool live = nb * 16 + r16 < a.R && r < a.R_all;
             const int i = live ? r / a.g : a.K - 1;
             const int lg = live ? r - (r / a.g) * a.g : 0;
             const uint16_t* qrow = a.q + ((size_t)(u.b * a.K + i) * a.Hq + u.hk * a.g + lg) * D;
@@ -352,7 +355,7 @@ template <int D>
 __device__ __forceinline__ void store_rows(const KernelArgs& a, const Unit& u, int r, bool final, const f32x4_t (&acc)[D / 16],
                                            float m, float l, int quad) {
     constexpr int DB = D / 16;
-    if (r >= a.R) return;
+    if (r >= a.R || u.rg * a.R + r >= a.R_all) return;
     f32x4_t acc_s[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc_s[db] = acc[db] * a.v_scale;  // a stored value stands for v_scale * v
@@ -366,7 +369,8 @@ __device__ __forceinline__ void store_rows(const KernelArgs& a, const Unit& u, i
         }
         return;
     }
-    const int i = r / a.g, h = u.hk * a.g + (r - (r / a.g) * a.g);
+    const int rk = u.rg * a.R + r;  // row in the kv head's R_all rows
+    const int i = rk / a.g, h = u.hk * a.g + (rk - (rk / a.g) * a.g);
     const size_t orow = (size_t)(u.b * a.K + i) * a.Hq + h;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -659,7 +663,7 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
             }
             w.template update<true>(s, vf, u.C, a.block_scale_log2, quad, a.block_p_mul);
         }
-        if (a.append) append_block<D, FP8>(a, u);
+        if (a.append && u.rg == 0) append_block<D, FP8>(a, u);
     }
     finish_unit(a, u, w, tg, wr, WT, WR, reinterpret_cast<float*>(lds));
 }
@@ -860,7 +864,7 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
         __syncthreads();
         w.hi_cap = u.N;
         compute_at(u.C, 0, std::true_type{});
-        if (a.append) append_block<D, FP8>(a, u);
+        if (a.append && u.rg == 0) append_block<D, FP8>(a, u);
     }
     finish_unit(a, u, w, 0, wave, 1, WR, reinterpret_cast<float*>(lds));
 }
@@ -877,8 +881,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const KernelArgs a) {
 
     const int tid = threadIdx.x;
     const int row = blockIdx.x;
-    const int pair = row / a.R, r = row - (row / a.R) * a.R;
-    const int b = pair / a.Hkv, hk = pair - (pair / a.Hkv) * a.Hkv;
+    // row = (request, kv head, row rk of its R_all rows); rk lives in row group rk / R.
+    const int head = row / a.R_all, rk = row - (row / a.R_all) * a.R_all;
+    const int b = head / a.Hkv, hk = head - (head / a.Hkv) * a.Hkv;
+    const int rg = rk / a.R, r = rk - rg * a.R;
+    const int pair = head * a.row_groups + rg;  // the units of that row group
     int u0, S;
     if (a.uniform_splits > 0) {  // units are laid out pair by pair: no table load
         S = a.uniform_splits;
@@ -888,7 +895,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const KernelArgs a) {
         S = a.pair_table[2 * pair + 1];
     }
     if (S <= 1) return;  // a single split wrote its output itself
-    const int i = r / a.g, l = r - (r / a.g) * a.g, h = hk * a.g + l;
+    const int i = rk / a.g, l = rk - (rk / a.g) * a.g, h = hk * a.g + l;
     const size_t orow = (size_t)(b * a.K + i) * a.Hq + h;
 
     // One pass: each thread folds its splits into a running (m, l, acc) state, so every

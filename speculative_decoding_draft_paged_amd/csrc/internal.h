@@ -7,7 +7,8 @@
 namespace blockattn {
 
 constexpr int kTileTokens = 32;   // keys per tile: one MFMA K-step of PV, two 16-token M blocks of QK^T
-constexpr int kMaxRowBlocks = 8;  // R = K * group <= 128 query rows per kv head
+constexpr int kMaxRowBlocks = 8;  // a work unit holds at most 128 query rows; more rows per kv head are
+                                   // split into row groups of at most 128, each its own unit
 constexpr int kMaxWaves = 8;      // wavefronts per workgroup of the attention kernels
 constexpr int kPidWindow = 2048;     // tiles whose page ids the streaming kernel stages in LDS at a time
 
@@ -15,7 +16,7 @@ constexpr int kPidWindow = 2048;     // tiles whose page ids the streaming kerne
 // the device from the live sequence length: unit s of S covers tiles tb + s*nt/S ..
 // tb + (s+1)*nt/S.
 struct WorkItem {
-    int32_t b, hk, s, S;
+    int32_t b, hk, s, S;  // hk: kv head * row_groups + row group
 };
 
 struct KernelArgs {
@@ -31,7 +32,9 @@ struct KernelArgs {
     float* part_acc;
     uint16_t* out;
     float* lse;
-    int32_t K, Hq, Hkv, g, R, P, stride, num_pages;
+    int32_t K, Hq, Hkv, g, R, P, stride, num_pages;  // R: query rows per work unit (<= 128)
+    int32_t R_all;         // query rows per kv head, K * g
+    int32_t row_groups;    // units of R rows that cover them: ceil(R_all / R)
     int32_t p_shift;       // log2 P
     int32_t window_left;   // -1: none
     int32_t window_right;  // -1: every later block key

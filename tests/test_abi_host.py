@@ -25,9 +25,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layouts_match_header():
-    # params: 12 int32 + 1 float = 52 bytes; info: 9 int32 + padding + size_t
+    # params: 13 int32 + 3 float = 64 bytes; info: 11 int32 + padding + size_t = 56 bytes
     assert ctypes.sizeof(ba.blockattn_params) == 64
-    assert ctypes.sizeof(ba.blockattn_plan_info_t) == 48
+    assert ctypes.sizeof(ba.blockattn_plan_info_t) == 56
 
 
 def params(**kw):
@@ -90,6 +90,21 @@ def test_tile_kernel_choice():
     assert plan_info(params(**w, block_size=1), [8193, 8193])["shared_tiles"] == 0  # R = 16
 
 
+def test_more_than_128_rows_run_as_row_groups():
+    w = dict(head_dim=128, page_size=64)
+    one = plan_info(params(**w, block_size=8, num_q_heads=16, num_kv_heads=1), [4000, 4000])  # R = 128
+    two = plan_info(params(**w, block_size=16, num_q_heads=16, num_kv_heads=1), [4000, 4000])  # R = 256
+    three = plan_info(params(**w, block_size=9, num_q_heads=32, num_kv_heads=2), [4000, 4000])  # R = 144
+    assert one["row_groups"] == 1 and two["row_groups"] == 2 and three["row_groups"] == 2
+    assert two["row_waves"] == 8 and three["row_waves"] == 5  # 144 rows: two groups of five row blocks
+    # every row group gets the same split count, so the units scale with the groups
+    forced = [plan_info(params(**w, block_size=k, num_q_heads=16, num_kv_heads=1, splits_override=3), [4000, 4000])
+              for k in (8, 16)]
+    assert forced[0]["units"] == 2 * 3 and forced[1]["units"] == 2 * 3 * 2
+    big = plan_info(params(**w, block_size=16, num_q_heads=64, num_kv_heads=2, batch=1), [9000])  # R = 512
+    assert big["row_groups"] == 4 and big["shared_tiles"] == 1
+
+
 def test_splits_override_and_clamp():
     info = plan_info(params(batch=1, splits_override=5), [1000])
     assert info["max_splits"] == 5 and info["units"] == 10
@@ -128,7 +143,6 @@ def test_workspace_size_grows_with_batch(B):
     (dict(page_size=512), [100, 100], ba.BLOCKATTN_ERR_UNSUPPORTED, "page_size"),
     (dict(num_q_heads=7), [100, 100], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "num_q_heads"),
     (dict(block_size=17), [100, 100], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "block_size"),
-    (dict(num_q_heads=40, num_kv_heads=1, block_size=4), [100, 100], ba.BLOCKATTN_ERR_UNSUPPORTED, "128"),
     (dict(), [6, 100], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "seq_lens[0]"),
     (dict(page_table_stride=3), [100, 97], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "page_table_stride"),
     (dict(window_left=0), [100, 100], ba.BLOCKATTN_ERR_INVALID_ARGUMENT, "window_left"),

@@ -91,6 +91,8 @@ CASES = [
     (14, dict(fp8=True, batch=2, K=2, hq=48, hkv=2, D=64, P=32, ctx=333, wl=40, wr=0)),   # shared tiles at D = 64, causal
     (15, dict(batch=2, K=7, hq=16, hkv=1, D=128, P=256, ctx=250, wl=1000, wr=-1)),   # 256-token pages, block over an edge
     (16, dict(fp8=True, batch=3, K=5, hq=8, hkv=1, D=64, P=256, ctx_range=(0, 700))),
+    (17, dict(batch=2, K=16, hq=16, hkv=1, D=128, P=32, ctx=600, wl=300, wr=-1)),   # R = 256: two row groups
+    (18, dict(fp8=True, batch=2, K=9, hq=32, hkv=2, D=64, P=64, ctx_range=(0, 400))),  # R = 144 at D = 64
 ]
 
 
@@ -133,7 +135,7 @@ def expected_append(inp, kb, vb):
     return k, v
 
 
-APPEND = [CASES[i] for i in (0, 2, 4, 5, 7, 8, 9, 10, 11, 12, 13)]
+APPEND = [CASES[i] for i in (0, 2, 4, 5, 7, 8, 9, 10, 11, 12, 13, 14, 15)]
 
 
 @pytest.mark.parametrize("idx,kw", APPEND, ids=[f"bk{i}" for i, _ in APPEND])

@@ -147,3 +147,8 @@ def test_fp8_config_case(name):
                          ids=["p256_stream", "p256_shared"])
 def test_fp8_pages_of_256_tokens(idx, kw):
     check_full(case8(idx, **kw), f"fp8 p256_{idx}")
+
+
+def test_fp8_more_than_128_rows():
+    c = case8(72, batch=2, K=16, hq=16, hkv=1, D=128, P=64, ctx=1100, wl=700, wr=-1)  # R = 256
+    check_full(c, "fp8 rows 256")

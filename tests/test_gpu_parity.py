@@ -200,3 +200,19 @@ PAGES_256 = [
 def test_pages_of_256_tokens(idx, kw):
     check_full(case(idx, **kw), f"p256_{idx}")
     check_full(case(idx, **kw), f"p256_{idx} splits=3", splits=3)
+
+
+# More than 128 query rows per kv head: row groups of at most 128 rows, each its own unit.
+ROW_GROUPS = [
+    (80, dict(batch=2, K=16, hq=16, hkv=1, D=128, P=64, ctx=900)),                          # R = 256: 2 x 128
+    (81, dict(batch=2, K=9, hq=32, hkv=2, D=128, P=32, ctx_range=(0, 700), wl=200, wr=-1)),  # R = 144, ragged
+    (82, dict(batch=1, K=16, hq=40, hkv=2, D=64, P=16, ctx=300, wl=64, wr=3)),              # R = 320: 3 groups
+    (83, dict(batch=3, K=12, hq=24, hkv=2, D=64, P=128, ctx_range=(10, 500))),              # R = 144 at D = 64
+]
+
+
+@pytest.mark.parametrize("idx,kw", ROW_GROUPS, ids=[f"rows_{i}" for i, _ in ROW_GROUPS])
+def test_more_than_128_rows(idx, kw):
+    _, _, info = check_full(case(idx, **kw), f"rows_{idx}")
+    assert info["row_groups"] > 1
+    check_full(case(idx, **kw), f"rows_{idx} splits=3", splits=3)

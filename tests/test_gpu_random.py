@@ -22,13 +22,13 @@ pytestmark = pytest.mark.gpu
 N_CASES = 96
 
 
-def draw(seed):
+def draw(seed, max_rows=128):
     rng = np.random.default_rng(7000 + seed)
     D = int(rng.choice([64, 128]))
     P = int(rng.choice([16, 32, 64, 128]))
     K = int(rng.integers(1, 17))
-    g = int(rng.integers(1, max(2, 128 // K + 1)))
-    g = max(1, min(g, 128 // K))
+    g = int(rng.integers(1, max(2, max_rows // K + 1)))
+    g = max(1, min(g, max_rows // K))
     hkv = int(rng.choice([1, 2, 4]))
     B = int(rng.integers(1, 5))
     lo = int(rng.integers(0, 400))
@@ -59,9 +59,8 @@ def block_arrays(c, seed):
     return mk(), mk()
 
 
-@pytest.mark.parametrize("seed", range(N_CASES))
-def test_random_shape(seed):
-    c, splits, waves, block = draw(seed)
+def run_case(seed, max_rows):
+    c, splits, waves, block = draw(seed, max_rows)
     print(f"rnd{seed}: K={c.block_size} Hq={c.num_q_heads} Hkv={c.num_kv_heads} D={c.head_dim} P={c.page_size} "
           f"B={c.batch} ctx={c.context_range} W={c.window_left}/{c.window_right} kv={c.kv_dtype} "
           f"scales={c.k_scale}/{c.v_scale} splits={splits} waves={waves} block={block}", flush=True)
@@ -86,3 +85,14 @@ def test_random_shape(seed):
         out, lse = o.float().cpu().numpy(), l.cpu().numpy()
         ref_out, ref_lse = oracle.attention_case(inp, k_block=kb, v_block=vb)
     H.compare(out, lse, ref_out, ref_lse, label=f"rnd{seed}")
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_shape(seed):
+    run_case(seed, 128)
+
+
+@pytest.mark.parametrize("seed", range(N_CASES, N_CASES + 24))
+def test_random_shape_up_to_512_rows(seed):
+    """Row groups: R up to 512 query rows per kv head."""
+    run_case(seed, 512)
