@@ -188,6 +188,25 @@ int blockattn_forward_block(blockattn_plan_t plan, const void* q, const void* k_
                             void* k_cache, void* v_cache, const int32_t* page_table, const int32_t* seq_lens,
                             void* workspace, void* out, float* lse, int32_t append, void* stream);
 
+/*
+ * Merge G partial results of the same rows computed over disjoint key sets, such as
+ * the shards of a context split across GPUs, after gathering each shard's out and LSE
+ * (the log-sum-exp merge of TensorRT-LLM PR #21130, Description item 1, taken over G
+ * parts): M = max_g lse_g, w_g = 2^(lse_g - M), out = sum_g w_g out_g / sum_g w_g,
+ * lse = M + log2 sum_g w_g. A part with lse = -inf holds no keys and weighs 0.
+ *   parts      G >= 1 (at most 4096)
+ *   rows       rows per part (B * K * Hq for forward results); 0 launches nothing
+ *   head_dim   64 or 128
+ *   part_out   bf16 [G, rows, head_dim], each part normalised (as forward returns it)
+ *   part_lse   fp32 [G, rows], base 2
+ *   out        bf16 [rows, head_dim]; must not overlap part_out
+ *   lse        fp32 [rows] or NULL
+ * Device pointers; launch only on stream (hipStream_t, NULL = default): no allocation,
+ * no host synchronisation.
+ */
+int blockattn_merge(int32_t parts, int64_t rows, int32_t head_dim, const void* part_out, const float* part_lse,
+                    void* out, float* lse, void* stream);
+
 /* Describe the plan (path taken, units, splits, future block keys on or off). */
 int blockattn_plan_info(blockattn_plan_t plan, blockattn_plan_info_t* info);
 

@@ -35,6 +35,7 @@ EXPORTED = (
     "blockattn_forward",
     "blockattn_windowed_forward",
     "blockattn_forward_block",
+    "blockattn_merge",
     "blockattn_plan_info",
     "blockattn_plan_set_profile_events",
     "blockattn_plan_destroy",
@@ -111,13 +112,15 @@ def load_library():
     lib.blockattn_forward.argtypes = fwd
     lib.blockattn_windowed_forward.argtypes = fwd
     lib.blockattn_forward_block.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp]
+    lib.blockattn_merge.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp, vp, vp, vp, vp]
     lib.blockattn_plan_info.argtypes = [vp, ctypes.POINTER(blockattn_plan_info_t)]
     lib.blockattn_plan_set_profile_events.argtypes = [vp, vp, vp]
     lib.blockattn_plan_destroy.argtypes = [vp]
     lib.blockattn_plan_destroy.restype = None
     lib.blockattn_last_error.restype = ctypes.c_char_p
     for name in ("blockattn_workspace_size", "blockattn_plan", "blockattn_forward", "blockattn_windowed_forward",
-                 "blockattn_forward_block", "blockattn_plan_info", "blockattn_plan_set_profile_events"):
+                 "blockattn_forward_block", "blockattn_merge", "blockattn_plan_info",
+                 "blockattn_plan_set_profile_events"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -299,3 +302,21 @@ def blockattn_forward_block(plan: Plan, q, k_block, v_block, k_cache, v_cache, p
         vp(plan.handle), vp(_ptr(q)), vp(_ptr(k_block)), vp(_ptr(v_block)), vp(_ptr(k_cache)), vp(_ptr(v_cache)),
         vp(_ptr(page_table)), vp(_ptr(seq_lens)), vp(_ptr(workspace)), vp(_ptr(out)), vp(_ptr(lse)),
         ctypes.c_int32(1 if append else 0), vp(_stream(stream))))
+
+
+def blockattn_merge(part_out, part_lse, out, lse=None, stream=None):
+    """G-way LSE merge: part_out bf16 [G, ..., D] and part_lse fp32 [G, ...] (base 2) into out [..., D] and lse."""
+    if part_out is None or part_lse is None:
+        raise ValueError("part_out and part_lse are required")
+    G = int(part_lse.shape[0])
+    rows = int(part_lse[0].numel()) if G > 0 else 0
+    D = int(part_out.shape[-1])
+    _expect("part_out", part_out, G * rows * D, ("bfloat16", "int16", "uint16"))
+    _expect("part_lse", part_lse, G * rows, ("float32",))
+    _expect("out", out, rows * D, ("bfloat16", "int16", "uint16"))
+    if lse is not None:
+        _expect("lse", lse, rows, ("float32",))
+    vp = ctypes.c_void_p
+    _check(load_library().blockattn_merge(ctypes.c_int32(G), ctypes.c_int64(rows), ctypes.c_int32(D),
+                                          vp(_ptr(part_out)), vp(_ptr(part_lse)), vp(_ptr(out)), vp(_ptr(lse)),
+                                          vp(_stream(stream))))

@@ -446,6 +446,28 @@ int blockattn_forward_block(blockattn_plan_t plan, const void* q, const void* k_
                        append);
 }
 
+int blockattn_merge(int32_t parts, int64_t rows, int32_t head_dim, const void* part_out, const float* part_lse,
+                    void* out, float* lse, void* stream) {
+    if (parts < 1 || parts > 4096) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "parts must be in [1, 4096]");
+    if (rows < 0) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "rows must be >= 0");
+    if (head_dim != 64 && head_dim != 128)
+        return fail(BLOCKATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (the gfx950 kernels are built for those)");
+    if (rows > (int64_t)0x7FFFFFFF * (256 / (head_dim / 8)))
+        return fail(BLOCKATTN_ERR_UNSUPPORTED, "rows exceed one launch; merge in pieces");
+    if (rows == 0) return BLOCKATTN_OK;
+    if (!part_out || !part_lse || !out)
+        return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "part_out, part_lse and out are required");
+    const char* po = static_cast<const char*>(part_out);
+    const char* oo = static_cast<const char*>(out);
+    const size_t part_bytes = (size_t)parts * rows * head_dim * 2, out_bytes = (size_t)rows * head_dim * 2;
+    if (oo < po + part_bytes && po < oo + out_bytes)
+        return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "out must not overlap part_out");
+    hipError_t e = launch_merge(head_dim, parts, rows, static_cast<const uint16_t*>(part_out), part_lse,
+                                static_cast<uint16_t*>(out), lse, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(BLOCKATTN_ERR_HIP, std::string("merge kernel launch: ") + hipGetErrorString(e));
+    return BLOCKATTN_OK;
+}
+
 int blockattn_plan_info(blockattn_plan_t plan, blockattn_plan_info_t* info) {
     if (!plan || !info) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "plan and info are required");
     info->kind = plan->kind;

@@ -945,6 +945,43 @@ struct LdsGrant {
     std::atomic<size_t> bytes[kLdsGrantDevices];  // static storage: starts at zero
 };
 
+// G-way log-sum-exp merge of normalised results of the same rows over disjoint key
+// sets (the combine a context-parallel split runs after gathering every shard's out
+// and base-2 LSE): M = max lse_g, w_g = 2^(lse_g - M), out = sum w_g out_g / sum w_g,
+// lse = M + log2 sum w_g. A part with no keys (lse = -inf) weighs 0; a NaN part makes
+// the row NaN. Each thread owns 8 elements (16 bytes) of one row.
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(int parts, int64_t rows, const uint16_t* part_out,
+                                                   const float* part_lse, uint16_t* out, float* lse) {
+    constexpr int TPR = D / 8;      // threads per row
+    constexpr int RPB = 256 / TPR;  // rows per workgroup
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+    const int c = (threadIdx.x % TPR) * 8;
+    if (row >= rows) return;
+    float M = kNegInf;
+    for (int g = 0; g < parts; ++g) M = fmaxf(M, part_lse[(int64_t)g * rows + row]);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
+    for (int g = 0; g < parts; ++g) {
+        const float lg = part_lse[(int64_t)g * rows + row];
+        const float w = lg == kNegInf ? 0.f : fast_exp2(lg - M);
+        const u32x4_t v = ldg16(part_out + ((int64_t)g * rows + row) * D + c);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            acc[2 * k] += w * __uint_as_float(v[k] << 16);
+            acc[2 * k + 1] += w * __uint_as_float(v[k] & 0xFFFF0000u);
+        }
+        L += w;
+    }
+    const float inv = L == 0.f ? 0.f : 1.f / L;  // no keys in any part: zeros; a NaN sum stays NaN
+    u32x4_t o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        o[k] = f32_to_bf16_rne(acc[2 * k] * inv) | ((uint32_t)f32_to_bf16_rne(acc[2 * k + 1] * inv) << 16);
+    *(u32x4_t*)(out + row * D + c) = o;
+    if (c == 0 && lse) lse[row] = L == 0.f ? kNegInf : M + log2f(L);
+}
+
 template <typename F>
 hipError_t launch_with_lds(F fn, int units, int threads, size_t lds, const KernelArgs& args, hipStream_t stream,
                            LdsGrant& grant) {

@@ -25,6 +25,21 @@ hipError_t launch_attention(const KernelShape& shape, bool windowed, int units, 
     return windowed ? dispatch<true, false>(shape, units, args, stream) : dispatch<false, false>(shape, units, args, stream);
 }
 
+hipError_t launch_merge(int head_dim, int parts, int64_t rows, const uint16_t* part_out, const float* part_lse,
+                        uint16_t* out, float* lse, hipStream_t stream) {
+    const int rpb = 256 / (head_dim / 8);
+    const int64_t blocks = (rows + rpb - 1) / rpb;
+    if (head_dim == 64)
+        hipLaunchKernelGGL(merge_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, parts, rows, part_out,
+                           part_lse, out, lse);
+    else if (head_dim == 128)
+        hipLaunchKernelGGL(merge_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, parts, rows, part_out,
+                           part_lse, out, lse);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 hipError_t launch_combine(int head_dim, int rows, const KernelArgs& args, hipStream_t stream) {
     if (head_dim == 64) hipLaunchKernelGGL(combine_kernel<64>, dim3(rows), dim3(256), 0, stream, args);
     else if (head_dim == 128) hipLaunchKernelGGL(combine_kernel<128>, dim3(rows), dim3(256), 0, stream, args);

@@ -197,3 +197,21 @@ def test_fp8_plan_keeps_the_bf16_shape():
         a = plan_info(params(**kw), [9000, 5000])
         b = plan_info(params(**kw, kv_dtype="fp8_e4m3", k_scale=0.0625, v_scale=0.0625), [9000, 5000])
         assert a == b
+
+
+def test_merge_checks_its_arguments():
+    lib = ba.load_library()
+    vp = ctypes.c_void_p
+    one, two = vp(0x1000), vp(0x100000)
+
+    def call(parts, rows, d, po=one, pl=one, out=two):
+        return lib.blockattn_merge(ctypes.c_int32(parts), ctypes.c_int64(rows), ctypes.c_int32(d), po, pl, out, None,
+                                   None)
+
+    assert call(0, 10, 64) == ba.BLOCKATTN_ERR_INVALID_ARGUMENT and "parts" in ba.blockattn_last_error()
+    assert call(2, -1, 64) == ba.BLOCKATTN_ERR_INVALID_ARGUMENT
+    assert call(2, 10, 96) == ba.BLOCKATTN_ERR_UNSUPPORTED and "head_dim" in ba.blockattn_last_error()
+    assert call(2, 0, 64, None, None, None) == ba.BLOCKATTN_OK  # nothing to merge, nothing launched
+    assert call(2, 10, 64, one, one, None) == ba.BLOCKATTN_ERR_INVALID_ARGUMENT
+    assert call(2, 10, 64, one, one, vp(0x1000 + 64)) == ba.BLOCKATTN_ERR_INVALID_ARGUMENT  # overlaps part_out
+    assert "overlap" in ba.blockattn_last_error()
