@@ -7,9 +7,9 @@
  * plus the K block keys, which are already appended to the cache.
  *
  *  - blockattn_forward: the non-causal unwindowed form. Every block query of a
- *    request sees the same N_b = seq_lens[b] keys (TensorRT-LLM PR #20374,
- *    "non-causal unwindowed DFlash block attention", Description: with no mask
- *    all block queries attend the same seq_lens_after keys).
+ *    request sees the same N_b = seq_lens[b] keys (TensorRT-LLM PR #20374, on
+ *    unwindowed DFlash block attention, Description: without a mask every block
+ *    query attends to all keys present after the append).
  *  - blockattn_windowed_forward: the non-causal windowed form: a causal
  *    windowed decode with a base-2 LSE, and the log-sum-exp merge of the block
  *    keys that follow each query (TensorRT-LLM PR #21130, DSpark non-causal
@@ -17,6 +17,10 @@
  *    the decode already streams, so the merge is done by the decode's own online
  *    softmax update rather than by a second pass. With K = 1 or window_right = 0
  *    no block key follows any query and the causal result is returned as is.
+ *  - blockattn_forward_block: either form with the block's own keys and values
+ *    taken from dense arrays, optionally appended to the cache in the same call.
+ *  - blockattn_merge: the log-sum-exp merge of partial results over disjoint key
+ *    sets, such as the shards of a context split across GPUs.
  *
  * Definitions (p = N_b - K + i is the absolute position of block query i):
  *   s_j  = sm_scale * <q[b,i,h,:], k_j>, with k_j read through the page table
