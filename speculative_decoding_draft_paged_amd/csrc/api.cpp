@@ -4,12 +4,13 @@
 // The plan replaces two host decisions of the pages' designs: the batch-size
 // gate between decode rows and context FMHA (TensorRT-LLM PR #20374,
 // Description: the row form wins at small batch because it gives multi-CTA
-// split-KV), and the split count of the paged split-KV kernel (PR #16150,
-// commits "rework flash-decoding style" and "pass the split count as a runtime
-// argument"). Here one kernel covers every batch: the plan sizes the split count
-// per request so that the partial kernel launches about two workgroups per
-// gfx950 compute unit (256 CUs), while every split keeps enough keys that its
-// fp32 partial state stays small next to the KV bytes it reads. The workspace is
+// split-KV), and the split count of the paged split-KV kernel (PR #16150, commit
+// list: a flash-decoding style rework whose split count became a runtime
+// argument). Here one kernel covers every batch: the plan picks the tiles per
+// split that minimise an estimated makespan over the workgroups the 256 gfx950
+// compute units hold at once (rounds of resident units, a fixed cost per unit,
+// and the combine launch when any request is split), so every split keeps enough
+// keys that its fp32 partial state stays small next to the KV bytes it reads. The workspace is
 // sized exactly and checked before anything launches, the lesson of PR #21130's
 // workspace item 3 (a stats carve that outgrew its buffer).
 #include "blockattn.h"

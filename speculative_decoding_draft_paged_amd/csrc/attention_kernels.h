@@ -36,9 +36,9 @@
 // its last-finishing unit needs an agent-scope release and acquire per unit; on
 // this part those cache write-backs cost far more than a second launch.)
 //
-// The split-KV form itself follows the flash-decoding rework of TensorRT-LLM
-// PR #16150 (paged DFlash cross-attention, commits "rework flash-decoding style"
-// and "split count as a runtime argument") and the multi-CTA split-KV of
+// The split-KV form itself follows TensorRT-LLM PR #16150 (paged DFlash
+// cross-attention; its commit list reworks the kernel flash-decoding style and
+// makes the split count a runtime argument) and the multi-CTA split-KV of
 // PR #20374, redone for 64-wide wavefronts, MFMA tiles and HND pages.
 #pragma once
 
