@@ -318,6 +318,37 @@ def pmc_summary(case_name, fetch_path, write_path):
     return out
 
 
+MFMA_COUNTERS = ("MfmaUtil", "VALUBusy", "LdsUtil", "GRBM_GUI_ACTIVE")
+
+
+def mfma_summary(case_name, path):
+    """Matrix-core, vector-ALU and LDS utilisation of the attention kernel from one rocprofv3
+    --pmc run of MFMA_COUNTERS (rocprofv3's derived metrics: MfmaUtil = MFMA-busy cycles
+    summed over SIMDs / (GPU-active cycles x SIMDs), in percent; VALUBusy and LdsUtil
+    likewise per CU), averaged over the attention-kernel dispatches of the run."""
+    out = {"case": case_name, "kernel_digest": kernel_source_digest()}
+    rows = _counter_rows(path)
+    for counter in MFMA_COUNTERS:
+        att = [v for k, c, v in rows if c == counter and ("stream_kernel" in k or "shared_kernel" in k)]
+        if not att:
+            raise SystemExit(f"{path}: no {counter} rows for the attention kernel")
+        out[counter] = round(sum(att) / len(att), 3)
+        out["dispatches"] = len(att)
+    return out
+
+
+def load_mfma(case_name: str):
+    """MfmaUtil (percent) of the attention kernel from a committed summary of the current kernels."""
+    path = os.path.join(ROOT, "profiles", f"pmc_mfma_{case_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_digest") != kernel_source_digest():
+        return None
+    return rec.get("MfmaUtil")
+
+
 def cpu_baseline(case, inp, gpu_out, kv_total, budget_s, blocks=None):
     """Time the fp64 oracle on a bounded sample of (request, kv head) pairs of the same call."""
     import numpy as np
@@ -379,12 +410,22 @@ def main():
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH", "WRITE"),
                     help="no GPU: read two rocprofv3 --pmc outputs (FETCH_SIZE, WRITE_SIZE) of a --copy-reference "
                          "run of --case (and --block) and write profiles/pmc_partial_<case>[_<block>].json")
+    ap.add_argument("--mfma-summary", metavar="PMC_DIR",
+                    help="no GPU: read a rocprofv3 --pmc run of " + " ".join(MFMA_COUNTERS) + " of --case (and "
+                         "--block) and write profiles/pmc_mfma_<case>[_<block>].json")
     args = ap.parse_args()
 
     label = args.case if args.block == "cache" else f"{args.case}_{args.block}"
     if args.pmc_summary:
         rec = pmc_summary(label, *args.pmc_summary)
         with open(os.path.join(ROOT, "profiles", f"pmc_partial_{label}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(json.dumps(rec))
+        return
+    if args.mfma_summary:
+        rec = mfma_summary(label, args.mfma_summary)
+        with open(os.path.join(ROOT, "profiles", f"pmc_mfma_{label}.json"), "w") as f:
             json.dump(rec, f, indent=1)
             f.write("\n")
         print(json.dumps(rec))
@@ -461,7 +502,8 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": ("shared_kernel" if res["shared_tiles"] else "stream_kernel") +
                                " (split-KV paged attention)",
-                     "kernel_us": round(res["partial_ms"] * 1e3, 2), "kernel_events": res["kernel_timing"]},
+                     "kernel_us": round(res["partial_ms"] * 1e3, 2), "kernel_events": res["kernel_timing"],
+                     "mfma_busy_pct": load_mfma(label)},
         "cpu_baseline": None,
     }
     if copy_ref is not None:

@@ -94,3 +94,20 @@ def test_counter_summary_scales_by_the_reference_copy(tmp_path):
     assert rec["write_bytes_per_launch"] == 10 * 1024
     assert rec["hbm_bytes_per_launch"] == rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
     assert rec["kernel_digest"] == bench.kernel_source_digest()
+
+
+def test_mfma_summary_averages_the_attention_kernel_only(tmp_path):
+    path = str(tmp_path / "m")
+    os.makedirs(path)
+    with open(os.path.join(path, "run_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for name, util in (("stream_kernel<64>", 6.0), ("stream_kernel<64>", 7.0), ("combine_kernel<64>", 50.0)):
+            for counter, value in (("MfmaUtil", util), ("VALUBusy", 2 * util), ("LdsUtil", util / 2),
+                                   ("GRBM_GUI_ACTIVE", 1000.0)):
+                w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+    rec = bench.mfma_summary("x", path)
+    assert rec["MfmaUtil"] == pytest.approx(6.5) and rec["VALUBusy"] == pytest.approx(13.0)
+    assert rec["LdsUtil"] == pytest.approx(3.25) and rec["dispatches"] == 2
+    assert rec["kernel_digest"] == bench.kernel_source_digest()
+
