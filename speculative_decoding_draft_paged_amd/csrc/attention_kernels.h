@@ -98,9 +98,9 @@ using Raw8 = typename std::conditional<FP8, u32x2_t, u32x4_t>::type;
 template <bool FP8>
 __device__ __forceinline__ Raw8<FP8> ldkv8(const void* pool, size_t e) {
     if constexpr (FP8)
-        return *(const u32x2_t*)(static_cast<const uint8_t*>(pool) + e);
+        return __builtin_nontemporal_load((const u32x2_t*)(static_cast<const uint8_t*>(pool) + e));
     else
-        return *(const u32x4_t*)(static_cast<const uint16_t*>(pool) + e);
+        return __builtin_nontemporal_load((const u32x4_t*)(static_cast<const uint16_t*>(pool) + e));
 }
 
 // OCP E4M3 of an fp32 value by round-to-nearest-even, saturating at +-448; NaN -> 0x7F.
