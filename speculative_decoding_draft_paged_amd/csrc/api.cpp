@@ -346,7 +346,7 @@ int run_forward(blockattn_plan_t plan, const void* q, const void* k, const void*
     if (e != hipSuccess) return fail(BLOCKATTN_ERR_HIP, std::string("attention kernel launch: ") + hipGetErrorString(e));
     if (plan->max_splits > 1) {
         const int rows = p.batch * p.num_kv_heads * plan->R_all;
-        e = launch_combine(p.head_dim, rows, ka, st);
+        e = launch_combine(p.head_dim, rows, plan->max_splits, ka, st);
         if (e != hipSuccess)
             return fail(BLOCKATTN_ERR_HIP, std::string("combine kernel launch: ") + hipGetErrorString(e));
     }

@@ -31,7 +31,7 @@
 // its request's only split writes the final bf16 output and base-2 LSE itself;
 // otherwise it writes its fp32 (acc, m, l) partial.
 //
-// combine_kernel: the LSE combine of the splits, one workgroup per output row,
+// combine_kernel: the LSE combine of the splits, several output rows per workgroup,
 // launched after the attention kernel. (Combining inside the attention kernel by
 // its last-finishing unit needs an agent-scope release and acquire per unit; on
 // this part those cache write-backs cost far more than a second launch.)
@@ -870,71 +870,97 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
 }
 
 // ---------------------------------------------------------------------------------
-// LSE combine of the splits: one workgroup per output row.
+// LSE combine of the splits. A row's D / 4 threads (4 floats each) form one split
+// stream; SL streams per row (a power of two, chosen from the largest split count so
+// that a thread folds at most about eight splits) and 256 / (D / 4 * SL) rows per
+// workgroup. With one stream a row's threads finish it from registers; with several,
+// the streams' states meet in LDS behind one barrier.
 template <int D>
-__global__ __launch_bounds__(256) void combine_kernel(const KernelArgs a) {
-    constexpr int DL = D / 4;     // threads per split row, 4 floats each
-    constexpr int SL = 256 / DL;  // split streams reduced in parallel
-    __shared__ float red_acc[SL][D];
-    __shared__ float red_l[SL];
-    __shared__ float red_m[SL];
+__global__ __launch_bounds__(256) void combine_kernel(const KernelArgs a, int SL, int rows) {
+    constexpr int DL = D / 4;        // threads per split stream, 4 floats each
+    constexpr int NS = 256 / DL;     // split streams per workgroup (SL per row)
+    __shared__ float red_acc[NS][D];
+    __shared__ float red_l[NS];
+    __shared__ float red_m[NS];
 
     const int tid = threadIdx.x;
-    const int row = blockIdx.x;
+    const int st = tid / DL, d4 = tid - st * DL;  // stream slot in the workgroup, column group
+    const int rl = st / SL, sl = st - rl * SL;      // row in the workgroup, stream of the row
+    const int row = blockIdx.x * (NS / SL) + rl;
     // row = (request, kv head, row rk of its R_all rows); rk lives in row group rk / R.
-    const int head = row / a.R_all, rk = row - (row / a.R_all) * a.R_all;
-    const int b = head / a.Hkv, hk = head - (head / a.Hkv) * a.Hkv;
-    const int rg = rk / a.R, r = rk - rg * a.R;
-    const int pair = head * a.row_groups + rg;  // the units of that row group
-    int u0, S;
-    if (a.uniform_splits > 0) {  // units are laid out pair by pair: no table load
-        S = a.uniform_splits;
-        u0 = pair * S;
-    } else {
-        u0 = a.pair_table[2 * pair];
-        S = a.pair_table[2 * pair + 1];
+    int u0 = 0, S = 0, r = 0;
+    size_t orow = 0;
+    if (row < rows) {
+        const int head = row / a.R_all, rk = row - (row / a.R_all) * a.R_all;
+        const int b = head / a.Hkv, hk = head - (head / a.Hkv) * a.Hkv;
+        const int rg = rk / a.R;
+        r = rk - rg * a.R;
+        const int pair = head * a.row_groups + rg;  // the units of that row group
+        if (a.uniform_splits > 0) {  // units are laid out pair by pair: no table load
+            S = a.uniform_splits;
+            u0 = pair * S;
+        } else {
+            u0 = a.pair_table[2 * pair];
+            S = a.pair_table[2 * pair + 1];
+        }
+        const int i = rk / a.g, l = rk - (rk / a.g) * a.g, h = hk * a.g + l;
+        orow = (size_t)(b * a.K + i) * a.Hq + h;
     }
-    if (S <= 1) return;  // a single split wrote its output itself
-    const int i = rk / a.g, l = rk - (rk / a.g) * a.g, h = hk * a.g + l;
-    const size_t orow = (size_t)(b * a.K + i) * a.Hq + h;
+    const bool active = S > 1;  // a single split wrote its output itself
 
-    // One pass: each thread folds its splits into a running (m, l, acc) state, so every
+    // Each thread folds its stream's splits into a running (m, l, acc) state, so every
     // load is independent of the others. A state with m = -inf (no keys) weighs 0, and
     // 0 * NaN still carries a NaN sum through.
-    const int d4 = tid % DL, sl = tid / DL;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     float m = kNegInf, lsum = 0.f;
+    if (active) {
 #pragma unroll 4
-    for (int s = sl; s < S; s += SL) {
-        const size_t pr = (size_t)(u0 + s) * a.R + r;
-        const float ms = a.part_m[pr];
-        const float ls = a.part_l[pr];
-        const f32x4_t as = *(const f32x4_t*)(a.part_acc + pr * D + 4 * d4);
-        const float mn = fmaxf(m, ms);
-        const float wa = m == kNegInf ? 0.f : fast_exp2(m - mn);
-        const float wb = ms == kNegInf ? 0.f : fast_exp2(ms - mn);
-        acc = acc * wa + as * wb;
-        lsum = lsum * wa + ls * wb;
-        m = mn;
+        for (int s = sl; s < S; s += SL) {
+            const size_t pr = (size_t)(u0 + s) * a.R + r;
+            const float ms = a.part_m[pr];
+            const float ls = a.part_l[pr];
+            const f32x4_t as = *(const f32x4_t*)(a.part_acc + pr * D + 4 * d4);
+            const float mn = fmaxf(m, ms);
+            const float wa = m == kNegInf ? 0.f : fast_exp2(m - mn);
+            const float wb = ms == kNegInf ? 0.f : fast_exp2(ms - mn);
+            acc = acc * wa + as * wb;
+            lsum = lsum * wa + ls * wb;
+            m = mn;
+        }
     }
-    *(f32x4_t*)&red_acc[sl][4 * d4] = acc;
-    if (d4 == 0) {
-        red_l[sl] = lsum;
-        red_m[sl] = m;
+    float M = m, L, wk;
+    f32x4_t o;
+    if (SL == 1) {
+        wk = m == kNegInf ? 0.f : fast_exp2(m - M);
+        L = wk * lsum;
+        o = acc * wk;
+    } else {
+        *(f32x4_t*)&red_acc[st][4 * d4] = acc;
+        if (d4 == 0) {
+            red_l[st] = lsum;
+            red_m[st] = m;
+        }
+        __syncthreads();
+        if (sl != 0) return;
+        const int s0 = rl * SL;
+        M = kNegInf;
+        for (int k = 0; k < SL; ++k) M = fmaxf(M, red_m[s0 + k]);
+        L = 0.f;
+        o = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < SL; ++k) {
+            wk = red_m[s0 + k] == kNegInf ? 0.f : fast_exp2(red_m[s0 + k] - M);
+            L += wk * red_l[s0 + k];
+            o += *(const f32x4_t*)&red_acc[s0 + k][4 * d4] * wk;
+        }
     }
-    __syncthreads();
-    float M = kNegInf;
+    if (!active) return;
+    float v[4];
 #pragma unroll
-    for (int k = 0; k < SL; ++k) M = fmaxf(M, red_m[k]);
-    float L = 0.f, o = 0.f;
-#pragma unroll
-    for (int k = 0; k < SL; ++k) {
-        const float wk = red_m[k] == kNegInf ? 0.f : fast_exp2(red_m[k] - M);
-        L += wk * red_l[k];
-        if (tid < D) o += wk * red_acc[k][tid];
-    }
-    if (tid < D) a.out[orow * D + tid] = f32_to_bf16_rne(L == 0.f ? 0.f : o / L);
-    if (tid == 0 && a.lse) a.lse[orow] = L == 0.f ? kNegInf : M + log2f(L);
+    for (int j = 0; j < 4; ++j) v[j] = L == 0.f ? 0.f : o[j] / L;  // no keys: zeros; a NaN sum stays NaN
+    const uint32_t lo = f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+    const uint32_t hi = f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+    *(u32x2_t*)(a.out + orow * D + 4 * d4) = u32x2_t{lo, hi};
+    if (d4 == 0 && a.lse) a.lse[orow] = L == 0.f ? kNegInf : M + log2f(L);
 }
 
 // Dynamic LDS above 64 KiB needs the kernel's limit raised, once per device (the

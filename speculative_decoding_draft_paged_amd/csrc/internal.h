@@ -72,7 +72,8 @@ hipError_t launch_attention(const KernelShape& shape, bool windowed, int units, 
 // fp8 E4M3 KV instantiations (kernels_fp8.hip); launch_attention routes to it when shape.fp8.
 hipError_t launch_attention_fp8(const KernelShape& shape, bool windowed, int units, const KernelArgs& args,
                                 hipStream_t stream);
-hipError_t launch_combine(int head_dim, int rows, const KernelArgs& args, hipStream_t stream);
+// LSE combine of the splits of `rows` output rows; max_splits: the largest split count of any row.
+hipError_t launch_combine(int head_dim, int rows, int max_splits, const KernelArgs& args, hipStream_t stream);
 // G-way LSE merge of bf16 partial results [parts, rows, head_dim] with base-2 LSEs [parts, rows].
 hipError_t launch_merge(int head_dim, int parts, int64_t rows, const uint16_t* part_out, const float* part_lse,
                         uint16_t* out, float* lse, hipStream_t stream);

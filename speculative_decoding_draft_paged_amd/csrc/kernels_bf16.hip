@@ -40,10 +40,17 @@ hipError_t launch_merge(int head_dim, int parts, int64_t rows, const uint16_t* p
     return hipGetLastError();
 }
 
-hipError_t launch_combine(int head_dim, int rows, const KernelArgs& args, hipStream_t stream) {
-    if (head_dim == 64) hipLaunchKernelGGL(combine_kernel<64>, dim3(rows), dim3(256), 0, stream, args);
-    else if (head_dim == 128) hipLaunchKernelGGL(combine_kernel<128>, dim3(rows), dim3(256), 0, stream, args);
-    else return hipErrorInvalidValue;
+hipError_t launch_combine(int head_dim, int rows, int max_splits, const KernelArgs& args, hipStream_t stream) {
+    if (head_dim != 64 && head_dim != 128) return hipErrorInvalidValue;
+    const int streams = 256 / (head_dim / 4);  // split streams per 256-thread workgroup
+    int sl = 1;                                 // streams per row: each folds at most about 8 splits
+    while (sl < streams && sl * 8 < max_splits) sl *= 2;
+    const int per_wg = streams / sl;
+    const unsigned blocks = (unsigned)((rows + per_wg - 1) / per_wg);
+    if (head_dim == 64)
+        hipLaunchKernelGGL(combine_kernel<64>, dim3(blocks), dim3(256), 0, stream, args, sl, rows);
+    else
+        hipLaunchKernelGGL(combine_kernel<128>, dim3(blocks), dim3(256), 0, stream, args, sl, rows);
     return hipGetLastError();
 }
 
