@@ -10,7 +10,8 @@ the plan splits a request's keys, the LSE combine.
 
 Timing: the K timed steps are one captured HIP graph, replayed between two
 device synchronisations; each step reads the next of M copies of the K/V pools
-(M * pool >= 1 GiB) so the 256 MB Infinity Cache cannot serve repeats. HIP
+(M * bytes read per call >= 1 GiB, M at most the step count) so the 256 MB
+Infinity Cache cannot serve repeats. HIP
 events recorded around every attention-kernel launch give that kernel's average
 duration (a separate pass of K eager calls), from which the roofline fraction is
 computed. HBM traffic per launch comes from a committed rocprofv3 counter summary
@@ -146,8 +147,15 @@ def run_case(case, steps, warmup, threads, graph=True, splits=0, waves=0, block=
     k0, v0 = kv(inp.k_pool), kv(inp.v_pool)
     pt = torch.from_numpy(inp.page_table).to(dev)
     lens = torch.from_numpy(inp.seq_lens).to(dev)
+    # Copies of the pools, rotated call by call, so that the calls between two reads of
+    # one copy read at least 1 GiB: the 256 MB Infinity Cache then cannot serve repeats.
+    # A call reads only its key sets (a windowed call far less than the pools hold), so
+    # the count follows the bytes read per call, up to one copy per timed call and 16 GiB
+    # of copies. Below about 50 MB per call the timed calls' whole read set fits the
+    # cache at the default step count; those cases are latency-bound either way.
     pool_bytes = 2 * inp.k_pool.nbytes
-    copies = max(1, math.ceil((1 << 30) / pool_bytes))
+    read_bytes = max(1, kv_bytes(case, inp.seq_lens, block))
+    copies = max(1, min(math.ceil((1 << 30) / read_bytes), max(steps, 1), (16 << 30) // pool_bytes))
     ks, vs = [k0], [v0]
     for _ in range(copies - 1):
         ks.append(k0.clone())

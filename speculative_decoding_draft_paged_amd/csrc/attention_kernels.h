@@ -786,7 +786,7 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
                 const int part = b / BP;
                 const char* base = static_cast<const char*>((part >> 1) ? a.vc : a.kc) +
                                    (((part & 1) ? slab1 : slab0) + (size_t)(b % BP) * RPB * D) * EB;
-                st.c[k] = *(const u32x4_t*)(base + lane_goff);
+                st.c[k] = __builtin_nontemporal_load((const u32x4_t*)(base + lane_goff));
             }
         };
         auto store = [&](const Stage& st, int t, int slot) {
