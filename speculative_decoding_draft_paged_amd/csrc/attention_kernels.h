@@ -616,13 +616,24 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
         };
 
         // Tile A's loads come first on every path into the loop head and tile B's right
-        // after, so each wait below names exactly one tile.
+        // after, so each wait below names exactly one tile. The loop runs while a third
+        // tile follows the pair, so every load it issues is a real tile; the last one or
+        // two tiles are consumed after it with no further loads (re-reading a clamped
+        // tile would fetch it from HBM again: the loads do not keep lines in the caches).
         TileRegs ta, tb;
         issue(ta, 0);
-        for (int k = 0; k < nk; k += 2) {
+        int k = 0;
+        for (; k + 2 < nk; k += 2) {
             issue(tb, k + 1);
             consume(ta, k, true, true);
-            consume(tb, k + 1, k + 1 < nk, false);
+            consume(tb, k + 1, true, false);
+        }
+        if (k + 1 < nk) {
+            issue(tb, k + 1);
+            consume(ta, k, true, false);
+            consume(tb, k + 1, true, false);
+        } else {
+            consume(ta, k, true, false);
         }
     }
     if (a.k_block != nullptr && u.s == u.S - 1) {
