@@ -489,9 +489,10 @@ __device__ void append_block(const KernelArgs& a, const Unit& u) {
 // workgroup stream interleaved tiles of the unit, two tiles in flight per wave.
 // The page ids of up to kPidWindow tiles are staged in LDS by the whole workgroup
 // (one gather round trip), so the tile loads depend only on short LDS reads. Every
-// global load of the loop sits at a fixed, unconditional place (tile indices past
-// the wave's last tile are clamped to it), which keeps the compiler's wait counts
-// exact: the wait for one tile never drains the tile behind it.
+// global load of the loop sits at a fixed, unconditional place, which keeps the
+// compiler's wait counts exact: the wait for one tile never drains the tile behind
+// it. The loop stops while a third tile still follows the pair in flight; the last
+// one or two tiles are consumed after it with no further loads.
 template <int D, int NBW, bool WINDOWED, bool ALL_ON, int MAXT, bool FP8>
 __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
     constexpr int KK = D / 32, DB = D / 16;
