@@ -90,17 +90,10 @@ __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? l
 
 __device__ __forceinline__ u32x4_t ldg16(const uint16_t* p) { return *(const u32x4_t*)p; }
 
-// Eight consecutive K or V elements starting at element `e` of a pool: 16 bytes of
-// bf16, or 8 bytes of fp8 E4M3.
+// Sixteen bytes of a pool starting at element `e`: 8 bf16 or 16 fp8 E4M3 elements.
 template <bool FP8>
-using Raw8 = typename std::conditional<FP8, u32x2_t, u32x4_t>::type;
-
-template <bool FP8>
-__device__ __forceinline__ Raw8<FP8> ldkv8(const void* pool, size_t e) {
-    if constexpr (FP8)
-        return __builtin_nontemporal_load((const u32x2_t*)(static_cast<const uint8_t*>(pool) + e));
-    else
-        return __builtin_nontemporal_load((const u32x4_t*)(static_cast<const uint16_t*>(pool) + e));
+__device__ __forceinline__ u32x4_t ldkv16(const void* pool, size_t e) {
+    return __builtin_nontemporal_load((const u32x4_t*)(static_cast<const char*>(pool) + e * (FP8 ? 1 : 2)));
 }
 
 // OCP E4M3 of an fp32 value by round-to-nearest-even, saturating at +-448; NaN -> 0x7F.
@@ -163,6 +156,14 @@ __device__ __forceinline__ float quad_sum(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// First of the 8 contraction elements that lane quad `quad` holds for K-step kk of a
+// 32-element MFMA step: 32 kk + 8 quad in order, or with `pair` 64 (kk / 2) + 16 quad +
+// 8 (kk % 2), so one 16-byte fp8 load of 16 consecutive elements feeds two steps.
+template <bool pair>
+__device__ __forceinline__ int kelem(int kk, int quad) {
+    return pair ? 64 * (kk >> 1) + 16 * quad + 8 * (kk & 1) : 32 * kk + 8 * quad;
+}
+
 // N keys, the last K of them the block (p = C + i); NC of them are read from the
 // cache (N, or C when the block comes from dense arrays); tiles [ulo, uhi).
 struct Unit {
@@ -214,6 +215,11 @@ struct WaveRows {
     int lo_max, hi_min;
     int hi_cap;  // keys at or past this come from elsewhere (the dense block) and are masked here
 
+    // kpair: the contraction elements of K-steps 2h and 2h + 1 are taken as lane quad's
+    // 16 consecutive elements 64h + 16 quad .. + 15 (first 8 to step 2h), so that one
+    // 16-byte load of 16 fp8 keys feeds two steps; the keys use the same layout. A dot
+    // product does not depend on the order of its terms, only on Q and K agreeing.
+    template <bool kpair = false>
     __device__ __forceinline__ void init(const KernelArgs& a, const Unit& u, int first_block, int lane) {
         const int r16 = lane & 15, quad = lane >> 4;
         const bool left_win = WINDOWED && a.window_left > 0;
@@ -230,7 +236,7 @@ struct WaveRows {
             const uint16_t* qrow = a.q + ((size_t)(u.b * a.K + i) * a.Hq + u.hk * a.g + lg) * D;
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
-                qf[n][kk] = __builtin_bit_cast(bf16x8_t, live ? ldg16(qrow + kk * 32 + quad * 8)
+                qf[n][kk] = __builtin_bit_cast(bf16x8_t, live ? ldg16(qrow + kelem<kpair>(kk, quad))
                                                               : u32x4_t{0u, 0u, 0u, 0u});
             const int p = u.C + i;
             row_lo[n] = left_win ? max(0, p - a.window_left + 1) : 0;
@@ -496,9 +502,14 @@ __device__ void append_block(const KernelArgs& a, const Unit& u) {
 template <int D, int NBW, bool WINDOWED, bool ALL_ON, int MAXT, bool FP8>
 __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
     constexpr int KK = D / 32, DB = D / 16;
-    constexpr int VCH = D / 16;   // 1-KiB chunks of the V tile (16 bytes per lane each)
-    constexpr int VP = kVPitch<D>;  // padded row pitch of the V tile in LDS (bf16 elements)
-    constexpr int RPC = 512 / D;  // tile rows per chunk
+    // Every K and V load is 16 bytes per lane: 8 bf16 elements, or 16 fp8 elements (the
+    // keys then in the paired contraction layout, so one load feeds two K-steps).
+    constexpr int KL = FP8 ? KK / 2 : KK;  // K loads per 16-row block
+    constexpr int VE = FP8 ? 16 : 8;       // V elements per lane load
+    constexpr int RPC = 64 * VE / D;       // tile rows per 1-KiB chunk (64 lanes x 16 bytes)
+    constexpr int VCH = T / RPC;           // chunks of the 32-row V tile
+    constexpr int VP = kVPitch<D>;         // padded row pitch of the V tile in LDS (bf16 elements)
+    static_assert(VCH * RPC == T && 16 % RPC == 0, "V chunks cover the tile and never straddle its halves");
 
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
     const int tid = threadIdx.x, nthreads = blockDim.x;
@@ -509,7 +520,7 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
     const int tg = wave / WR, wr = wave - (wave / WR) * WR;  // token group, row group
     const Unit u = decode_unit<WINDOWED>(a);
     WaveRows<D, NBW, WINDOWED, ALL_ON> w;
-    w.init(a, u, wr * NBW, lane);
+    w.template init<FP8>(a, u, wr * NBW, lane);
     // LDS: [one V tile per wave] [page-id window]
     uint16_t* vlds = lds + (size_t)wave * T * VP;
     int* pid_tab = reinterpret_cast<int*>(lds + (size_t)WT * WR * T * VP);
@@ -519,8 +530,8 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
     const int pmask = (1 << a.p_shift) - 1;
 
     struct TileRegs {
-        Raw8<FP8> k[2][KK];
-        Raw8<FP8> v[VCH];
+        u32x4_t k[2][KL];
+        u32x4_t v[VCH];
     };
 
     for (int win = u.ulo; win < u.uhi; win += kPidWindow) {
@@ -559,14 +570,14 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int kk = 0; kk < KK; ++kk)
-                    t.k[mb][kk] = ldkv8<FP8>(a.kc, (mb ? base1 : base0) + (size_t)r16 * D + kk * 32 + quad * 8);
+                for (int kl = 0; kl < KL; ++kl)
+                    t.k[mb][kl] = ldkv16<FP8>(a.kc, (mb ? base1 : base0) + (size_t)r16 * D + kelem<FP8>(FP8 ? 2 * kl : kl, quad));
 #pragma unroll
             for (int c = 0; c < VCH; ++c) {
-                const int row = c * RPC + (lane * 8) / D;  // tile row of this lane's 16 bytes
-                const int col = (lane * 8) % D;
+                const int row = c * RPC + (lane * VE) / D;  // tile row of this lane's 16 bytes
+                const int col = (lane * VE) % D;
                 const bool h1 = c * RPC >= 16;
-                t.v[c] = ldkv8<FP8>(a.vc, (h1 ? base1 : base0) + (size_t)(row - (h1 ? 16 : 0)) * D + col);
+                t.v[c] = ldkv16<FP8>(a.vc, (h1 ? base1 : base0) + (size_t)(row - (h1 ? 16 : 0)) * D + col);
             }
         };
 
@@ -574,26 +585,41 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
             const int t0 = (win + tg + k * WT) * T;
             f32x4_t s[NBW][2];
             if (valid) {
-                if (t0 + T > u.NC) {  // the tail tile: rows past the cached keys become zeros
+                // V rows into the wave's LDS tile, as bf16; on the tail tile rows past the
+                // cached keys become zeros
+                auto put_v = [&](bool tail) {
 #pragma unroll
                     for (int c = 0; c < VCH; ++c) {
-                        const int row = c * RPC + (lane * 8) / D;
-                        const int col = (lane * 8) % D;
-                        *(u32x4_t*)(vlds + row * VP + col) = (t0 + row < u.NC) ? widen8(t.v[c]) : u32x4_t{0u, 0u, 0u, 0u};
+                        const int row = c * RPC + (lane * VE) / D;
+                        const int col = (lane * VE) % D;
+                        const bool zero = tail && t0 + row >= u.NC;
+                        const u32x4_t z = {0u, 0u, 0u, 0u};
+                        if constexpr (FP8) {
+                            const u32x4_t lo = widen8(u32x2_t{t.v[c].x, t.v[c].y});
+                            const u32x4_t hi = widen8(u32x2_t{t.v[c].z, t.v[c].w});
+                            *(u32x4_t*)(vlds + row * VP + col) = zero ? z : lo;
+                            *(u32x4_t*)(vlds + row * VP + col + 8) = zero ? z : hi;
+                        } else {
+                            *(u32x4_t*)(vlds + row * VP + col) = zero ? z : t.v[c];
+                        }
                     }
-                } else {
-#pragma unroll
-                    for (int c = 0; c < VCH; ++c) {
-                        const int row = c * RPC + (lane * 8) / D;
-                        const int col = (lane * 8) % D;
-                        *(u32x4_t*)(vlds + row * VP + col) = widen8(t.v[c]);
-                    }
-                }
+                };
+                if (t0 + T > u.NC)
+                    put_v(true);
+                else
+                    put_v(false);
                 bf16x8_t kf[2][KK];
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                    for (int kk = 0; kk < KK; ++kk) kf[mb][kk] = __builtin_bit_cast(bf16x8_t, widen8(t.k[mb][kk]));
+                    for (int kl = 0; kl < KL; ++kl) {
+                        if constexpr (FP8) {
+                            kf[mb][2 * kl] = __builtin_bit_cast(bf16x8_t, widen8(u32x2_t{t.k[mb][kl].x, t.k[mb][kl].y}));
+                            kf[mb][2 * kl + 1] = __builtin_bit_cast(bf16x8_t, widen8(u32x2_t{t.k[mb][kl].z, t.k[mb][kl].w}));
+                        } else {
+                            kf[mb][kl] = __builtin_bit_cast(bf16x8_t, t.k[mb][kl]);
+                        }
+                    }
                 w.scores(kf, s);
             }
             if (reissue) issue(t, k + 2);  // the registers are free again: keep two tiles in flight
@@ -651,12 +677,12 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk) {
                     const int i = mb * 16 + r16;
-                    kf[mb][kk] = __builtin_bit_cast(bf16x8_t, i < a.K ? ldg16(kb + i * rstride + kk * 32 + quad * 8)
+                    kf[mb][kk] = __builtin_bit_cast(bf16x8_t, i < a.K ? ldg16(kb + i * rstride + kelem<FP8>(kk, quad))
                                                                      : u32x4_t{0u, 0u, 0u, 0u});
                 }
 #pragma unroll
-            for (int c = 0; c < VCH; ++c) {
-                const int row = c * RPC + (lane * 8) / D;
+            for (int c = 0; c < D / 16; ++c) {  // 8 bf16 elements per lane
+                const int row = c * (512 / D) + (lane * 8) / D;
                 const int col = (lane * 8) % D;
                 *(u32x4_t*)(vlds + row * VP + col) = row < a.K ? ldg16(vb + row * rstride + col) : u32x4_t{0u, 0u, 0u, 0u};
             }
