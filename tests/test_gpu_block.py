@@ -93,6 +93,10 @@ CASES = [
     (16, dict(fp8=True, batch=3, K=5, hq=8, hkv=1, D=64, P=256, ctx_range=(0, 700))),
     (17, dict(batch=2, K=16, hq=16, hkv=1, D=128, P=32, ctx=600, wl=300, wr=-1)),   # R = 256: two row groups
     (18, dict(fp8=True, batch=2, K=9, hq=32, hkv=2, D=64, P=64, ctx_range=(0, 400))),  # R = 144 at D = 64
+    # fp8 pools through the streaming kernel at D = 128 (paired contraction layout, two 16-byte K
+    # loads per row block): unwindowed R = 16, and windowed R = 30 with mixed lengths
+    (19, dict(fp8=True, batch=2, K=2, hq=16, hkv=2, D=128, P=64, ctx=700, ks=0.25, vs=0.5)),
+    (20, dict(fp8=True, batch=3, K=3, hq=30, hkv=3, D=128, P=32, ctx_range=(0, 900), wl=200, wr=-1)),
 ]
 
 
