@@ -910,7 +910,7 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
 // ---------------------------------------------------------------------------------
 // LSE combine of the splits. A row's D / 4 threads (4 floats each) form one split
 // stream; SL streams per row (a power of two, chosen from the largest split count so
-// that a thread folds at most about eight splits) and 256 / (D / 4 * SL) rows per
+// that a thread folds at most about four splits) and 256 / (D / 4 * SL) rows per
 // workgroup. With one stream a row's threads finish it from registers; with several,
 // the streams' states meet in LDS behind one barrier.
 template <int D>

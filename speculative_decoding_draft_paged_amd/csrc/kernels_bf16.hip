@@ -43,8 +43,8 @@ hipError_t launch_merge(int head_dim, int parts, int64_t rows, const uint16_t* p
 hipError_t launch_combine(int head_dim, int rows, int max_splits, const KernelArgs& args, hipStream_t stream) {
     if (head_dim != 64 && head_dim != 128) return hipErrorInvalidValue;
     const int streams = 256 / (head_dim / 4);  // split streams per 256-thread workgroup
-    int sl = 1;                                 // streams per row: each folds at most about 8 splits
-    while (sl < streams && sl * 8 < max_splits) sl *= 2;
+    int sl = 1;                                 // streams per row: each folds at most about 4 splits
+    while (sl < streams && sl * 4 < max_splits) sl *= 2;
     const int per_wg = streams / sl;
     const unsigned blocks = (unsigned)((rows + per_wg - 1) / per_wg);
     if (head_dim == 64)

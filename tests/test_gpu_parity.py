@@ -219,20 +219,21 @@ def test_more_than_128_rows(idx, kw):
 
 
 # The split combine packs 256 / (D / 4 * SL) output rows into a workgroup, with SL split
-# streams per row chosen from the largest split count (1 up to 8 splits, 2 up to 16, ...,
+# streams per row chosen from the largest split count (1 up to 4 splits, 2 up to 8, ...,
 # at most 16 at D = 64 and 8 at D = 128). Each case forces a split count that selects one
 # SL, with a row count that leaves the last workgroup partly empty; the mixed-length
 # cases give requests different split counts (the per-pair table instead of a uniform S).
 COMBINE = [
     # (idx, splits, kwargs)
     (70, 2, dict(batch=3, K=3, hq=10, hkv=2, D=64, P=32, ctx=900)),              # SL 1, 90 rows over 16 per group
-    (71, 12, dict(batch=2, K=7, hq=6, hkv=2, D=64, P=32, ctx=3000)),             # SL 2, 84 rows
-    (72, 30, dict(batch=1, K=5, hq=6, hkv=3, D=64, P=16, ctx=4000)),             # SL 4
-    (73, 60, dict(batch=1, K=7, hq=8, hkv=2, D=64, P=32, ctx=5000)),             # SL 8
-    (74, 130, dict(batch=1, K=3, hq=4, hkv=1, D=64, P=32, ctx=8000)),            # SL 16, one row per group
-    (75, 5, dict(batch=3, K=1, hq=12, hkv=1, D=128, P=64, ctx=2500)),            # SL 1 at D = 128, 36 rows
+    (71, 6, dict(batch=2, K=7, hq=6, hkv=2, D=64, P=32, ctx=3000)),              # SL 2, 84 rows over 8
+    (72, 30, dict(batch=1, K=5, hq=3, hkv=3, D=64, P=16, ctx=4000)),             # SL 8, 15 rows over 2
+    (73, 60, dict(batch=1, K=7, hq=8, hkv=2, D=64, P=32, ctx=5000)),             # SL 16
+    (74, 130, dict(batch=1, K=3, hq=4, hkv=1, D=64, P=32, ctx=8000)),            # SL 16, 33 splits per stream
+    (75, 3, dict(batch=3, K=1, hq=12, hkv=1, D=128, P=64, ctx=2500)),            # SL 1 at D = 128, 36 rows over 8
     (76, 40, dict(batch=2, K=1, hq=16, hkv=1, D=128, P=64, ctx=3000)),           # SL 8 at D = 128
-    (77, 9, dict(batch=3, K=5, hq=6, hkv=2, D=64, P=32, ctx_range=(20, 600))),   # mixed split counts, SL 2
+    (79, 7, dict(batch=2, K=3, hq=10, hkv=2, D=128, P=64, ctx=2000)),            # SL 2 at D = 128, 60 rows over 4
+    (77, 9, dict(batch=3, K=5, hq=6, hkv=2, D=64, P=32, ctx_range=(20, 600))),   # mixed split counts, SL 4
     (78, 3, dict(batch=3, K=3, hq=48, hkv=3, D=128, P=64, ctx_range=(0, 700), wl=200, wr=-1)),  # shared tiles
 ]
 
