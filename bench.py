@@ -8,18 +8,22 @@ data from the seeded generator. One step = one blockattn_forward call for the
 whole batch (plan once, outside timing): the paged attention kernel and, when
 the plan splits a request's keys, the LSE combine.
 
-Timing: the K timed steps are one captured HIP graph, replayed between two
-device synchronisations; each step reads the next of M copies of the K/V pools
-(M * bytes read per call >= 1 GiB, M at most the step count) so the 256 MB
-Infinity Cache cannot serve repeats. HIP
-events recorded around every attention-kernel launch give that kernel's average
-duration (a separate pass of K eager calls), from which the roofline fraction is
-computed. HBM traffic per launch comes from a committed rocprofv3 counter summary
-of the same kernel source (null when the source has changed since).
+Timing: the K timed steps are one captured HIP graph, replayed R >= 10 times,
+each replay between two device synchronisations and timed with HIP events; the
+per-call time is the median replay / K. Each step reads the next of M copies of
+the K/V pools (M * bytes read per call >= 1 GiB, M at most the step count) so
+the 256 MB Infinity Cache cannot serve repeats. HIP events recorded around every
+attention-kernel launch give that kernel's average duration (a separate pass of
+K eager calls), from which the roofline fraction is computed. HBM traffic per
+launch comes from a committed rocprofv3 counter summary of the same kernel
+source (null when the source has changed since).
 
 Output: one JSON line (metric, value in GB/s of algorithmic KV bytes, ...,
-roofline, cpu_baseline). The cpu_baseline leg times the fp64 oracle on a
-bounded sample of the same workload on the host cores.
+roofline, cpu_baseline, read_reference, cases). The cpu_baseline leg times the
+fp64 oracle on a bounded sample of the same workload on the host cores;
+read_reference is the read-only streaming kernel over 2 GiB (the achievable HBM
+read rate); cases repeats the measurement for every 128K-context configuration
+case (per-call time, kernel time, fraction of 8 TB/s).
 """
 from __future__ import annotations
 
@@ -126,7 +130,7 @@ def load_traffic(case_name: str, per_launch_bytes: int):
     return rec.get("hbm_bytes_per_launch")
 
 
-def run_case(case, steps, warmup, threads, graph=True, splits=0, waves=0, block="cache"):
+def run_case(case, steps, warmup, threads, graph=True, splits=0, waves=0, block="cache", replays=10):
     import numpy as np
     import torch
 
@@ -207,21 +211,27 @@ def run_case(case, steps, warmup, threads, graph=True, splits=0, waves=0, block=
             log(f"[bench] graph capture unavailable ({e}); timing eager launches")
             torch.cuda.synchronize()
 
-    # Timed region: exactly `steps` forward calls between two device synchronisations.
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    hip.hip.hipEventRecord(ctypes.c_void_p(ga), ctypes.c_void_p(stream.cuda_stream))
-    if used_graph:
-        g.replay()
-    else:
-        for i in range(steps):
-            step(i)
-    hip.hip.hipEventRecord(ctypes.c_void_p(gb), ctypes.c_void_p(stream.cuda_stream))
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
+    # Timed regions: `replays` runs of exactly `steps` forward calls (one graph replay, or the
+    # eager calls), each between two device synchronisations and timed with HIP events on the
+    # launch stream; the per-call time is the median over the runs.
+    run_ms, walls = [], []
+    for _ in range(max(1, replays)):
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        hip.hip.hipEventRecord(ctypes.c_void_p(ga), ctypes.c_void_p(stream.cuda_stream))
+        if used_graph:
+            g.replay()
+        else:
+            for i in range(steps):
+                step(i)
+        hip.hip.hipEventRecord(ctypes.c_void_p(gb), ctypes.c_void_p(stream.cuda_stream))
+        torch.cuda.synchronize()
+        walls.append(time.perf_counter() - t_start)
+        run_ms.append(hip.elapsed_ms(ga, gb))
     if not torch.equal(out, ref_out):
         raise RuntimeError("timed run output differs from the warm-up output")
-    total_ms = hip.elapsed_ms(ga, gb)
+    total_ms = float(np.median(run_ms))
+    wall = float(np.median(walls))
 
     # Kernel timing: HIP events recorded by the library right around every attention-kernel
     # launch, on the stream it launches on, over `steps` eager calls.
@@ -240,6 +250,9 @@ def run_case(case, steps, warmup, threads, graph=True, splits=0, waves=0, block=
         "kv_bytes": kv_bytes(case, inp.seq_lens, block),
         "block": block,
         "step_ms": total_ms / steps,
+        "step_ms_min": min(run_ms) / steps,
+        "step_ms_max": max(run_ms) / steps,
+        "replays": len(run_ms),
         "wall_ms": wall * 1e3 / steps,
         "partial_ms": sum(kern_ms) / len(kern_ms),
         "partial_ms_min": min(kern_ms),
@@ -254,6 +267,45 @@ def run_case(case, steps, warmup, threads, graph=True, splits=0, waves=0, block=
     }
     plan.destroy()
     return res, inp, out, blocks
+
+
+READ_BYTES = 2 << 30  # the read-only streaming reference reads 2 GiB per launch
+
+
+def read_reference(reps=20):
+    """The read-only streaming reference: blockattn_stream_read over 2 GiB (every byte read once with
+    the attention kernels' 16-byte non-temporal loads), median of `reps` launches timed with HIP
+    events, at three launch widths; the best median is the box's achievable HBM read rate."""
+    import numpy as np
+    import torch
+
+    import speculative_decoding_draft_paged_amd as ba
+
+    src = torch.ones(READ_BYTES // 4, dtype=torch.int32, device="cuda")
+    acc = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hip = HipEvents()
+    evs = hip.create(2 * reps)
+    stream = torch.cuda.current_stream().cuda_stream
+    best = None
+    for wg in (1024, 2048, 4096):
+        for _ in range(3):
+            ba.blockattn_stream_read(src, acc, wg)
+        torch.cuda.synchronize()
+        for r in range(reps):
+            hip.hip.hipEventRecord(ctypes.c_void_p(evs[2 * r]), ctypes.c_void_p(stream))
+            ba.blockattn_stream_read(src, acc, wg)
+            hip.hip.hipEventRecord(ctypes.c_void_p(evs[2 * r + 1]), ctypes.c_void_p(stream))
+        torch.cuda.synchronize()
+        us = float(np.median([hip.elapsed_ms(evs[2 * r], evs[2 * r + 1]) for r in range(reps)])) * 1e3
+        if best is None or us < best["us"]:
+            best = {"kernel": "blockattn_stream_read, 2 GiB read once (16-byte non-temporal loads)", "workgroups": wg,
+                    "us": round(us, 1), "gbs": round(READ_BYTES / (us * 1e-6) / 1e9, 1), "reps": reps}
+    hip.destroy(evs)
+    best["frac_of_peak"] = round(best["gbs"] / HBM_PEAK_GBS, 4)
+    del src, acc
+    torch.cuda.empty_cache()
+    log(f"[bench] read reference: {best}")
+    return best
 
 
 COPY_ELEMS = 1 << 28  # float32 elements of the reference copy: 1 GiB read + 1 GiB written per launch
@@ -398,6 +450,49 @@ def cpu_baseline(case, inp, gpu_out, kv_total, budget_s, blocks=None):
     }
 
 
+def case_list(spec):
+    """Names of the per-case array: the ten 128K-context cases by default."""
+    from synth.configs import all_cases
+
+    if spec == "none":
+        return []
+    if spec == "128k":
+        return [c.name for c in all_cases() if c.context == 131072]
+    if spec == "all":
+        return [c.name for c in all_cases()]
+    return [n for n in spec.split(",") if n]
+
+
+def per_case_array(names, head_case, head_res, args, threads):
+    """One entry per case: median per-call time over graph replays, the attention kernel's HIP-event
+    time, and both as GB/s of algorithmic KV bytes and as a fraction of 8 TB/s. The headline case is
+    not run again."""
+    import torch
+
+    from synth.configs import find_case
+
+    rows = []
+    for name in names:
+        c = find_case(name)
+        if name == head_case.name and args.block == "cache" and not args.splits and not args.waves:
+            r = head_res
+        else:
+            r, _, _, _ = run_case(c, args.case_steps, 3, threads, graph=not args.eager, replays=args.replays)
+            torch.cuda.empty_cache()
+        gbs = r["kv_bytes"] / (r["step_ms"] * 1e-3) / 1e9
+        kgbs = r["kv_bytes"] / (r["partial_ms"] * 1e-3) / 1e9
+        row = {"case": name, "kv_dtype": c.kv_dtype, "batch": c.batch, "context": c.context, "kv_bytes": r["kv_bytes"],
+               "us_per_call": round(r["step_ms"] * 1e3, 2), "gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+               "kernel_us": round(r["partial_ms"] * 1e3, 2), "kernel_frac": round(kgbs / HBM_PEAK_GBS, 4),
+               "us_min": round(r["step_ms_min"] * 1e3, 2), "us_max": round(r["step_ms_max"] * 1e3, 2),
+               "steps": args.case_steps if r is not head_res else args.steps, "replays": r["replays"],
+               "units": r["units"], "max_splits": r["max_splits"], "combine_launch": r["combine_launch"]}
+        rows.append(row)
+        log(f"[case] {name:16s} {row['us_per_call']:9.2f} us/call  {gbs:7.0f} GB/s  ({100 * row['frac']:5.1f} % of 8 TB/s)"
+            f"  kernel {row['kernel_us']:9.2f} us ({100 * row['kernel_frac']:5.1f} %)  units {row['units']}")
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -413,6 +508,13 @@ def main():
     ap.add_argument("--block", choices=("cache", "dense", "append"), default="cache",
                     help="where the block's keys and values come from: the cache (default), dense arrays, or "
                          "dense arrays also appended into the cache in the same call")
+    ap.add_argument("--replays", type=int, default=10,
+                    help="timed runs of the K steps (graph replays); the per-call time is their median")
+    ap.add_argument("--cases", default="128k",
+                    help="per-case array in the same line: '128k' (the ten 128K-context cases, default), 'all', "
+                         "'none', or a comma-separated list of case names")
+    ap.add_argument("--case-steps", type=int, default=20, help="calls per timed run for the per-case array")
+    ap.add_argument("--no-read-reference", action="store_true", help="skip the read-only 2 GiB streaming reference")
     ap.add_argument("--copy-reference", action="store_true",
                     help="also time a plain 1 GiB elementwise copy (achievable HBM rate; PMC calibration kernel)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH", "WRITE"),
@@ -452,7 +554,7 @@ def main():
 
     case = find_case(args.case)
     res, inp, out, blocks = run_case(case, args.steps, args.warmup, threads, graph=not args.eager,
-                                     splits=args.splits, waves=args.waves, block=args.block)
+                                     splits=args.splits, waves=args.waves, block=args.block, replays=args.replays)
     kvb = res["kv_bytes"]
     value = kvb / (res["step_ms"] * 1e-3) / 1e9
     achieved = kvb / (res["partial_ms"] * 1e-3) / 1e9
@@ -467,7 +569,7 @@ def main():
             if case.kv_dtype != "bf16":
                 c = fp8_variant(c, case.k_scale, case.v_scale)
             r, _, _, _ = run_case(c, max(10, args.steps // 2), 3, threads, graph=not args.eager,
-                                  splits=args.splits, waves=args.waves, block=args.block)
+                                  splits=args.splits, waves=args.waves, block=args.block, replays=args.replays)
             r["gbs"] = r["kv_bytes"] / (r["step_ms"] * 1e-3) / 1e9
             r["frac"] = r["gbs"] / HBM_PEAK_GBS
             r["partial_gbs"] = r["kv_bytes"] / (r["partial_ms"] * 1e-3) / 1e9
@@ -478,6 +580,7 @@ def main():
             torch.cuda.empty_cache()
 
     copy_ref = copy_reference() if args.copy_reference else None
+    read_ref = None if args.no_read_reference else read_reference()
     traffic = load_traffic(label, kvb)
     line = {
         "metric": METRIC,
@@ -494,7 +597,7 @@ def main():
         "vs_baseline": (round(value / PAGES_CONTEXT[case.name], 3) if case.name in PAGES_CONTEXT else None),
         "vs_baseline_note": "ratio to the pages' SM107 decode-row figure for the same shape (another GPU: context)"
                             if case.name in PAGES_CONTEXT else None,
-        "dtype": "bf16",
+        "dtype": case.kv_dtype,
         "data": "synthetic",
         "config": {"workload": f"{case.name}: draft-block attention, {case.num_q_heads}q/{case.num_kv_heads}kv heads, "
                                f"head_dim {case.head_dim}, K={case.block_size}, page {case.page_size}, "
@@ -514,12 +617,18 @@ def main():
                      "mfma_busy_pct": load_mfma(label)},
         "cpu_baseline": None,
     }
+    if read_ref is not None:
+        line["read_reference"] = read_ref
     if copy_ref is not None:
         line["copy_reference"] = copy_ref
     if sweep is not None:
         line["sweep"] = [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()} for r in sweep]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, inp, out, kvb, args.cpu_seconds, blocks)
+    del inp, out, blocks
+    names = case_list(args.cases)
+    if names:
+        line["cases"] = per_case_array(names, case, res, args, threads)
     print(json.dumps(line), flush=True)
 
 

@@ -123,23 +123,38 @@ typedef struct blockattn_plan_info {
 
 /*
  * Exact workspace bytes needed for these parameters and host lengths: the
- * split-KV work list, the per-(request, kv head) table and the fp32 partial
- * softmax states (acc, m, l) of every work unit.
- * seq_lens_host: int32 [B] on the host. Returns BLOCKATTN_OK and sets *bytes.
+ * split-KV work list, the per-(request, kv head) table, the input-error word and
+ * the fp32 partial softmax states (acc, m, l) of every work unit. The size is
+ * computed from the same plan a forward runs, so the softmax statistics can never
+ * outgrow their carve (TensorRT-LLM PR #21130, Description item 3: the workspace
+ * must hold the stats, and a launch is refused when it is too small).
+ * seq_lens_host: int32 [B] on the host. Returns BLOCKATTN_OK and sets *bytes;
+ * invalid parameters give the same errors as blockattn_plan.
  */
 int blockattn_workspace_size(const blockattn_params* params, const int32_t* seq_lens_host, size_t* bytes);
 
 /*
  * Validate, choose the split-KV decomposition for gfx950 and lay out the
- * workspace. seq_lens_host fixes the split counts; forward reads the live
- * lengths from device memory, so the lengths may change between forwards (for
- * example under graph replay) as long as every N_b stays in
- * [K, page_table_stride * P].
+ * workspace: the planning step of the pages' multi-CTA split-KV decode
+ * (TensorRT-LLM PR #20374, Description: decode rows take the paged split-KV
+ * path with its counter buffers; PR #16150, commit list: the split count of the
+ * paged context kernel is a runtime argument). seq_lens_host fixes the split
+ * counts; forward reads the live lengths from device memory, so the lengths may
+ * change between forwards (for example under graph replay) as long as every
+ * N_b stays in [K, page_table_stride * P]. A live length outside that range is
+ * clamped into it and recorded in the input-error word (blockattn_input_errors).
  * workspace: device buffer of workspace_bytes, or NULL for a host-only plan
  * (info and validation only; such a plan cannot run). With a workspace, one
  * asynchronous host-to-device copy of the work list is enqueued on stream
  * (a hipStream_t, NULL = default stream). The plan must outlive that copy;
  * blockattn_plan_destroy waits for it.
+ * Streams: a forward on that same stream is ordered after the copy by the
+ * stream. A forward on another stream first waits for the copy on the device
+ * (an event wait, no host synchronisation). A forward captured into a graph on
+ * another stream cannot wait on the copy's event: the copy must have completed
+ * before such a capture begins (for example after synchronising the plan's
+ * stream; torch.cuda.graph synchronises the device when capture starts).
+ * A plan is not safe for concurrent use from several host threads.
  * On success *plan holds a new plan owned by the caller.
  */
 int blockattn_plan(const blockattn_params* params, const int32_t* seq_lens_host, void* workspace,
@@ -151,6 +166,11 @@ int blockattn_plan(const blockattn_params* params, const int32_t* seq_lens_host,
  * seq_lens: int32 device buffers; workspace: the buffer given to the plan;
  * out: bf16 [B, K, Hq, D]; lse: fp32 [B, K, Hq] or NULL; stream: hipStream_t.
  * Launch only: no allocation, no host synchronisation.
+ * Out-of-range device inputs never lead to reads outside the caller's buffers:
+ * a page id outside [0, num_pages) is clamped into that range and a length
+ * outside [K, page_table_stride * P] into that one. The result is then not the
+ * one the inputs describe, and the clamp is recorded in the workspace's
+ * input-error word, which blockattn_input_errors reads.
  */
 int blockattn_forward(blockattn_plan_t plan, const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* page_table, const int32_t* seq_lens, void* workspace, void* out, float* lse,
@@ -211,8 +231,36 @@ int blockattn_forward_block(blockattn_plan_t plan, const void* q, const void* k_
 int blockattn_merge(int32_t parts, int64_t rows, int32_t head_dim, const void* part_out, const float* part_lse,
                     void* out, float* lse, void* stream);
 
-/* Describe the plan (path taken, units, splits, future block keys on or off). */
+/*
+ * Describe the plan: the path taken (kernel, units, splits, whether a combine
+ * launch follows, whether the block keys after each query are merged). Tests use it
+ * to assert which path runs, as the pages' tests count the calls of each
+ * path (TensorRT-LLM PR #20374, Test Coverage: the row path is checked by counting
+ * which kernels a step calls). Returns BLOCKATTN_ERR_INVALID_ARGUMENT for NULL
+ * arguments; reads only the host plan.
+ */
 int blockattn_plan_info(blockattn_plan_t plan, blockattn_plan_info_t* info);
+
+/* Bits of the input-error word. */
+enum {
+    BLOCKATTN_INPUT_BAD_LENGTH = 1, /* a device seq_lens entry was outside [K, page_table_stride * P] */
+    BLOCKATTN_INPUT_BAD_PAGE = 2    /* a page-table entry a call read was outside [0, num_pages) */
+};
+
+/*
+ * Checked mode for debugging callers: report which out-of-range device inputs the
+ * forwards on this plan's workspace met since the last call (or since the plan
+ * was made), then clear the record. The forwards clamp such inputs so that no read
+ * leaves the caller's buffers. The pages ask that a bad shape raise a clear,
+ * actionable error (TensorRT-LLM PR #16150, commit list); this is that rule for the
+ * inputs only the device sees.
+ *   workspace  the buffer given to the plan
+ *   stream     the stream the forwards ran on (hipStream_t); the call is ordered
+ *              after them, waits on the host for the read-back, and must not be
+ *              made during graph capture
+ *   flags      receives BLOCKATTN_INPUT_BAD_LENGTH | BLOCKATTN_INPUT_BAD_PAGE, or 0
+ */
+int blockattn_input_errors(blockattn_plan_t plan, void* workspace, void* stream, int32_t* flags);
 
 /*
  * Profiling aid. When before/after are non-NULL hipEvent_t handles, every later
@@ -221,6 +269,21 @@ int blockattn_plan_info(blockattn_plan_t plan, blockattn_plan_info_t* info);
  * alone with hipEventElapsedTime. Pass NULL, NULL to stop. Adds no device work.
  */
 int blockattn_plan_set_profile_events(blockattn_plan_t plan, void* before, void* after);
+
+/*
+ * Measurement aid: the read-only streaming reference. Reads every byte of src once
+ * with the 16-byte non-temporal vector loads the attention kernels use for K and V
+ * and XOR-folds the words into *result (so no load is dropped); writes nothing
+ * else. Timed over a buffer far larger than the caches (2 GiB), it gives the HBM
+ * read rate a plain kernel reaches, the yardstick for the attention kernels' KV
+ * read rate.
+ *   src         device buffer, 16-byte aligned
+ *   bytes       a positive multiple of 16
+ *   result      device uint32; the caller zeroes it first if it wants the fold's value
+ *   workgroups  256-thread workgroups to launch (0: 2048, eight per compute unit)
+ *   stream      hipStream_t. Launch only: no allocation, no host synchronisation.
+ */
+int blockattn_stream_read(const void* src, size_t bytes, uint32_t* result, int32_t workgroups, void* stream);
 
 /* Wait for the plan's pending work-list copy, then free it. NULL is ignored. */
 void blockattn_plan_destroy(blockattn_plan_t plan);

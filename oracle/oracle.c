@@ -90,12 +90,18 @@ uint16_t oracle_encode_kv(int kv_dtype, float scale, uint16_t bits) {
         }
         return sign | (uint16_t)best;
     }
-    /* bf16 of q by round-to-nearest-even: the nearest bf16 above or below */
+    /* bf16 of q by round-to-nearest-even (IEEE 754 roundTiesToEven into 8 significand
+       bits): the nearer of the two bf16 values around q, the one with an even code on a
+       tie. lo is q cut to bf16 and hi the next code away from zero. Past the largest
+       finite bf16 (0x7F7F) the next step is infinity, which rounding weighs as the value
+       2^128: a magnitude at or beyond the midpoint 2^128 (1 - 2^-9) becomes infinity.
+       Every NaN becomes the one quiet NaN 0x7FC0. */
     if (isnan(q)) return 0x7FC0;
     uint32_t u;
     memcpy(&u, &q, sizeof u);
     const uint16_t lo = (uint16_t)(u >> 16), hi = (uint16_t)(lo + 1);
-    const double dq = (double)q, dlo = oracle_bf16_to_double(lo), dhi = oracle_bf16_to_double(hi);
+    const double dq = (double)q, dlo = oracle_bf16_to_double(lo);
+    const double dhi = (hi & 0x7F80) == 0x7F80 ? copysign(ldexp(1.0, 128), dq) : oracle_bf16_to_double(hi);
     if ((u & 0xFFFFu) == 0) return lo;
     const double elo = fabs(dq - dlo), ehi = fabs(dhi - dq);
     if (elo < ehi) return lo;

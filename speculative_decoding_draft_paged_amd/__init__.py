@@ -28,6 +28,8 @@ BLOCKATTN_ERR_PLAN_MISMATCH = 4
 BLOCKATTN_ERR_HIP = 5
 BLOCKATTN_KV_BF16 = 0
 BLOCKATTN_KV_FP8_E4M3 = 1
+BLOCKATTN_INPUT_BAD_LENGTH = 1
+BLOCKATTN_INPUT_BAD_PAGE = 2
 
 EXPORTED = (
     "blockattn_workspace_size",
@@ -38,6 +40,8 @@ EXPORTED = (
     "blockattn_merge",
     "blockattn_plan_info",
     "blockattn_plan_set_profile_events",
+    "blockattn_input_errors",
+    "blockattn_stream_read",
     "blockattn_plan_destroy",
     "blockattn_last_error",
 )
@@ -115,12 +119,14 @@ def load_library():
     lib.blockattn_merge.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp, vp, vp, vp, vp]
     lib.blockattn_plan_info.argtypes = [vp, ctypes.POINTER(blockattn_plan_info_t)]
     lib.blockattn_plan_set_profile_events.argtypes = [vp, vp, vp]
+    lib.blockattn_input_errors.argtypes = [vp, vp, vp, i32p]
+    lib.blockattn_stream_read.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_int32, vp]
     lib.blockattn_plan_destroy.argtypes = [vp]
     lib.blockattn_plan_destroy.restype = None
     lib.blockattn_last_error.restype = ctypes.c_char_p
     for name in ("blockattn_workspace_size", "blockattn_plan", "blockattn_forward", "blockattn_windowed_forward",
                  "blockattn_forward_block", "blockattn_merge", "blockattn_plan_info",
-                 "blockattn_plan_set_profile_events"):
+                 "blockattn_plan_set_profile_events", "blockattn_input_errors", "blockattn_stream_read"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -233,6 +239,24 @@ def blockattn_plan_set_profile_events(plan: Plan, before, after):
     """Record raw hipEvent_t handles (ints) around the partial kernel of later forwards; None stops."""
     _check(load_library().blockattn_plan_set_profile_events(ctypes.c_void_p(plan.handle), ctypes.c_void_p(before),
                                                             ctypes.c_void_p(after)))
+
+
+def blockattn_input_errors(plan: Plan, workspace, stream=None) -> int:
+    """Out-of-range device inputs met since the last call (BLOCKATTN_INPUT_* bits); clears the record."""
+    flags = ctypes.c_int32(0)
+    _check(load_library().blockattn_input_errors(ctypes.c_void_p(plan.handle), ctypes.c_void_p(_ptr(workspace)),
+                                                 ctypes.c_void_p(_stream(stream)), ctypes.byref(flags)))
+    return int(flags.value)
+
+
+def blockattn_stream_read(src, result, workgroups=0, stream=None):
+    """Read-only streaming reference over the bytes of `src` (a device tensor); XOR fold into `result`."""
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    _expect("result", result, 1, ("int32", "uint32"))
+    vp = ctypes.c_void_p
+    _check(load_library().blockattn_stream_read(vp(_ptr(src)), src.numel() * src.element_size(), vp(_ptr(result)),
+                                                ctypes.c_int32(workgroups), vp(_stream(stream))))
 
 
 def blockattn_plan_destroy(plan: Plan):

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libblockattn.so")
 
-SOURCES = ["api.cpp", "kernels_bf16.hip", "kernels_fp8.hip"]
+SOURCES = ["api.cpp", "kernels_bf16.hip", "kernels_fp8.hip", "stream_read.hip"]
 HEADERS = ["internal.h", "attention_kernels.h"]
 
 HIPCC_FLAGS = [

@@ -39,17 +39,20 @@ int fail(int code, const std::string& msg) {
 }
 
 constexpr int kNumCUs = 256;
+constexpr size_t kReadback = 256;  // pinned bytes after the staged head, for reading the error word back
 constexpr size_t kLdsPerCU = 160 * 1024;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Workspace sections, each 256-byte aligned. The head (work list, pair table and the
+// input-error word) is what the plan uploads; the partials follow it.
 struct Layout {
-    size_t work = 0, pairs = 0, m = 0, l = 0, acc = 0, total = 0;
+    size_t work = 0, pairs = 0, err = 0, m = 0, l = 0, acc = 0, total = 0;
 };
 
-
-
 }  // namespace
+
+int blockattn::record_error(int code, const char* msg) { return fail(code, msg); }
 
 struct blockattn_plan_s {
     blockattn_params prm{};
@@ -65,8 +68,10 @@ struct blockattn_plan_s {
     Layout lay;
     void* ws = nullptr;
     bool uploaded = false;
-    void* stage = nullptr;
-    hipEvent_t copy_done = nullptr;
+    void* stage = nullptr;             // pinned host copy of the workspace head, then 256 bytes of read-back
+    hipEvent_t copy_done = nullptr;    // recorded after the head's upload on upload_stream
+    hipStream_t upload_stream = nullptr;
+    bool upload_seen_done = false;     // copy_done has been observed complete: no stream needs to wait on it
     hipEvent_t prof_before = nullptr, prof_after = nullptr;
 };
 
@@ -268,7 +273,8 @@ int build_plan(const blockattn_params* p, const int32_t* lens, blockattn_plan_s*
     Layout& L = pl->lay;
     L.work = 0;
     L.pairs = align_up(L.work + pl->work.size() * sizeof(WorkItem), 256);
-    L.m = align_up(L.pairs + pl->pair_table.size() * sizeof(int32_t), 256);
+    L.err = align_up(L.pairs + pl->pair_table.size() * sizeof(int32_t), 256);
+    L.m = align_up(L.err + sizeof(uint32_t), 256);
     L.l = align_up(L.m + (size_t)pl->units * pl->R * sizeof(float), 256);
     L.acc = align_up(L.l + (size_t)pl->units * pl->R * sizeof(float), 256);
     L.total = align_up(L.acc + (size_t)pl->units * pl->R * p->head_dim * sizeof(float), 256);
@@ -293,6 +299,25 @@ int check_forward(blockattn_plan_t plan, int kind, const void* q, const void* k,
     return BLOCKATTN_OK;
 }
 
+// A forward on a stream other than the one the plan uploaded its work list on must not
+// start before that copy has landed. Outside graph capture it waits on the copy's event
+// (on the device, no host wait) until the copy has once been seen complete. A stream
+// being captured cannot wait on an event recorded outside the capture; the header makes
+// the copy's completion before such a capture the caller's part.
+hipError_t order_after_upload(blockattn_plan_t plan, hipStream_t st) {
+    if (plan->upload_seen_done || st == plan->upload_stream) return hipSuccess;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(st, &cs);
+    if (e != hipSuccess || cs != hipStreamCaptureStatusNone) return e;
+    e = hipEventQuery(plan->copy_done);
+    if (e == hipSuccess) {
+        plan->upload_seen_done = true;
+        return hipSuccess;
+    }
+    if (e != hipErrorNotReady) return e;
+    return hipStreamWaitEvent(st, plan->copy_done, 0);
+}
+
 int run_forward(blockattn_plan_t plan, const void* q, const void* k, const void* v, const int32_t* pt,
                 const int32_t* lens, void* ws, void* out, float* lse, void* stream, const void* k_block = nullptr,
                 const void* v_block = nullptr, int append = 0) {
@@ -315,6 +340,7 @@ int run_forward(blockattn_plan_t plan, const void* q, const void* k, const void*
     ka.part_m = reinterpret_cast<float*>(base + plan->lay.m);
     ka.part_l = reinterpret_cast<float*>(base + plan->lay.l);
     ka.part_acc = reinterpret_cast<float*>(base + plan->lay.acc);
+    ka.err = reinterpret_cast<uint32_t*>(base + plan->lay.err);
     ka.out = static_cast<uint16_t*>(out);
     ka.lse = lse;
     ka.K = p.block_size;
@@ -339,7 +365,8 @@ int run_forward(blockattn_plan_t plan, const void* q, const void* k, const void*
     ka.block_scale_log2 = (float)((double)p.sm_scale * 1.4426950408889634);
     ka.block_p_mul = 1.0f / p.v_scale;
 
-    hipError_t e = hipSuccess;
+    hipError_t e = order_after_upload(plan, st);
+    if (e != hipSuccess) return fail(BLOCKATTN_ERR_HIP, std::string("ordering after the work-list upload: ") + hipGetErrorString(e));
     if (plan->prof_before) e = hipEventRecord(plan->prof_before, st);
     if (e == hipSuccess) e = launch_attention(plan->shape, plan->kind == 1, plan->units, ka, st);
     if (e == hipSuccess && plan->prof_after) e = hipEventRecord(plan->prof_after, st);
@@ -386,8 +413,8 @@ int blockattn_plan(const blockattn_params* params, const int32_t* seq_lens_host,
             delete pl;
             return fail(BLOCKATTN_ERR_WORKSPACE_TOO_SMALL, buf);
         }
-        const size_t head = pl->lay.m;  // work list and pair table
-        hipError_t e = hipHostMalloc(&pl->stage, head, hipHostMallocDefault);
+        const size_t head = pl->lay.m;  // work list, pair table and the cleared input-error word
+        hipError_t e = hipHostMalloc(&pl->stage, head + kReadback, hipHostMallocDefault);
         if (e != hipSuccess) {
             delete pl;
             return fail(BLOCKATTN_ERR_HIP, std::string("hipHostMalloc: ") + hipGetErrorString(e));
@@ -406,6 +433,7 @@ int blockattn_plan(const blockattn_params* params, const int32_t* seq_lens_host,
         }
         pl->ws = workspace;
         pl->uploaded = true;
+        pl->upload_stream = st;
     }
     *plan = pl;
     g_last_error.clear();
@@ -492,6 +520,27 @@ int blockattn_plan_set_profile_events(blockattn_plan_t plan, void* before, void*
         return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "pass both profiling events or neither");
     plan->prof_before = static_cast<hipEvent_t>(before);
     plan->prof_after = static_cast<hipEvent_t>(after);
+    return BLOCKATTN_OK;
+}
+
+int blockattn_input_errors(blockattn_plan_t plan, void* workspace, void* stream, int32_t* flags) {
+    if (!plan || !flags) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "plan and flags are required");
+    *flags = 0;
+    if (!plan->uploaded || workspace != plan->ws)
+        return fail(BLOCKATTN_ERR_PLAN_MISMATCH, "workspace is not the one this plan was uploaded to");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(st, &cs);
+    if (e == hipSuccess && cs != hipStreamCaptureStatusNone)
+        return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "blockattn_input_errors waits on the host: call it outside graph capture");
+    uint32_t* host = reinterpret_cast<uint32_t*>(static_cast<char*>(plan->stage) + plan->lay.m);
+    char* word = static_cast<char*>(workspace) + plan->lay.err;
+    if (e == hipSuccess) e = order_after_upload(plan, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(host, word, sizeof(uint32_t), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipMemsetAsync(word, 0, sizeof(uint32_t), st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(BLOCKATTN_ERR_HIP, std::string("reading the input-error word: ") + hipGetErrorString(e));
+    *flags = (int32_t)*host;
     return BLOCKATTN_OK;
 }
 

@@ -77,9 +77,12 @@ constexpr int kVPitch = D + 16;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// fp32 -> bf16 by round-to-nearest-even. Carrying into the exponent field rounds a magnitude at
+// or past the midpoint between the largest finite bf16 and 2^128 to infinity; every NaN becomes
+// the canonical quiet NaN 0x7FC0.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
     uint32_t u = __float_as_uint(x);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)0x7FC0u;
     u += 0x7FFFu + ((u >> 16) & 1u);
     return (uint16_t)(u >> 16);
 }
@@ -87,6 +90,22 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// Record an input that had to be clamped (a device length or a page id out of range) in the
+// workspace's input-error word. The clamp keeps every read inside the caller's buffers; the
+// word lets a caller find out that the result is not the one its inputs describe.
+__device__ __forceinline__ void flag_input_error(uint32_t* err, uint32_t bits) {
+    __hip_atomic_fetch_or(err, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Page id entry `v` of a page-table row, clamped into [0, num_pages).
+__device__ __forceinline__ int checked_page(const KernelArgs& a, int v) {
+    if ((unsigned)v >= (unsigned)a.num_pages) {
+        flag_input_error(a.err, kErrPage);
+        v = clampi(v, 0, a.num_pages - 1);
+    }
+    return v;
+}
 
 __device__ __forceinline__ u32x4_t ldg16(const uint16_t* p) { return *(const u32x4_t*)p; }
 
@@ -189,7 +208,9 @@ __device__ __forceinline__ Unit decode_unit(const KernelArgs& a) {
     u.rg = wi.hk - u.hk * a.row_groups;
     u.s = wi.s;
     u.S = wi.S;
-    u.N = clampi(a.seq_lens[wi.b], a.K, a.stride * a.P);
+    const int n_dev = a.seq_lens[wi.b];
+    u.N = clampi(n_dev, a.K, a.stride * a.P);
+    if (u.N != n_dev && threadIdx.x == 0) flag_input_error(a.err, kErrLength);
     u.C = u.N - a.K;
     u.NC = a.k_block ? u.C : u.N;
     const int key_lo = (WINDOWED && a.window_left > 0) ? max(0, u.C - a.window_left + 1) : 0;
@@ -478,7 +499,7 @@ __device__ void append_block(const KernelArgs& a, const Unit& u) {
         const int e = isv ? idx - n : idx;
         const int i = e / D, d = e - (e / D) * D;
         const int j = u.C + i;
-        const int page = clampi(pt_row[j >> a.p_shift], 0, a.num_pages - 1);
+        const int page = checked_page(a, pt_row[j >> a.p_shift]);
         const size_t off = (((size_t)page * a.Hkv + u.hk) << (a.p_shift + kLog2<D>)) + (size_t)(j & pmask) * D + d;
         const uint16_t xb = (isv ? a.v_block : a.k_block)[((size_t)(u.b * a.K + i) * a.Hkv + u.hk) * D + d];
         const float q = bf16_to_f32(xb) / (isv ? a.v_scale : a.k_scale);
@@ -551,7 +572,7 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int j = j0 + e * nthreads + tid;
-                    if (j < n) pid_tab[j] = clampi(v[e], 0, a.num_pages - 1) * a.Hkv + u.hk;
+                    if (j < n) pid_tab[j] = checked_page(a, v[e]) * a.Hkv + u.hk;
                 }
             }
         }
@@ -799,7 +820,7 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int j = j0 + e * NT + tid;
-                    if (j < n) pid_tab[j] = clampi(v[e], 0, a.num_pages - 1) * a.Hkv + u.hk;
+                    if (j < n) pid_tab[j] = checked_page(a, v[e]) * a.Hkv + u.hk;
                 }
             }
         }

@@ -12,6 +12,10 @@ constexpr int kMaxRowBlocks = 8;  // a work unit holds at most 128 query rows; m
 constexpr int kMaxWaves = 8;      // wavefronts per workgroup of the attention kernels
 constexpr int kPidWindow = 2048;     // tiles whose page ids the streaming kernel stages in LDS at a time
 
+// Bits of the input-error word (the values of BLOCKATTN_INPUT_BAD_LENGTH / _BAD_PAGE).
+constexpr uint32_t kErrLength = 1u;  // a device length outside [K, stride * P]: clamped into it
+constexpr uint32_t kErrPage = 2u;    // a page id read outside [0, num_pages): clamped into it
+
 // One unit of split-KV work. Tiles [lo, hi) of the key range of (b, h_kv) are derived on
 // the device from the live sequence length: unit s of S covers tiles tb + s*nt/S ..
 // tb + (s+1)*nt/S.
@@ -30,6 +34,7 @@ struct KernelArgs {
     float* part_m;
     float* part_l;
     float* part_acc;
+    uint32_t* err;         // input-error word: bits kErrLength / kErrPage are set when a clamp was needed
     uint16_t* out;
     float* lse;
     int32_t K, Hq, Hkv, g, R, P, stride, num_pages;  // R: query rows per work unit (<= 128)
@@ -74,6 +79,9 @@ hipError_t launch_attention_fp8(const KernelShape& shape, bool windowed, int uni
                                 hipStream_t stream);
 // LSE combine of the splits of `rows` output rows; max_splits: the largest split count of any row.
 hipError_t launch_combine(int head_dim, int rows, int max_splits, const KernelArgs& args, hipStream_t stream);
+// Set the calling thread's last-error text (blockattn_last_error) and return code.
+int record_error(int code, const char* msg);
+
 // G-way LSE merge of bf16 partial results [parts, rows, head_dim] with base-2 LSEs [parts, rows].
 hipError_t launch_merge(int head_dim, int parts, int64_t rows, const uint16_t* part_out, const float* part_lse,
                         uint16_t* out, float* lse, hipStream_t stream);

@@ -7,6 +7,8 @@ and its bf16 / float8_e4m3fn casts; the dense block to identities (arrays equal
 to the cache give the cache's result exactly; writing the arrays into a bf16
 cache gives the same result) and to the brute force.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -52,6 +54,54 @@ def test_encode_bf16_matches_library(scale):
     want = (x / torch.tensor(scale, dtype=torch.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     got = np.array([oracle.encode_kv("bf16", scale, int(b)) for b in bits], dtype=np.uint16)
     np.testing.assert_array_equal(got, want)
+
+
+def _bf16_bits(values):
+    return torch.tensor(values, dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_encode_bf16_overflow_matches_library():
+    """Quotients near FLT_MAX: past the midpoint between the largest finite bf16 and 2^128
+    they round to infinity, below it to 0x7F7F (torch's fp32 -> bf16 cast decides)."""
+    top = [0x7F7F, 0x7F7E, 0x7F70, 0x7F00, 0xFF7F, 0xFF7E, 0xFF00]
+    scales = [1.0, 0.999, 0.998, 0.9975, 0.997, 0.996, 0.99, 0.9, 0.75, 0.5, 0.25, 1.01]
+    hit_inf = hit_top = 0
+    for s in scales:
+        bits = np.array(top, dtype=np.uint16)
+        x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float32)
+        want = (x / torch.tensor(s, dtype=torch.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        got = np.array([oracle.encode_kv("bf16", s, int(b)) for b in bits], dtype=np.uint16)
+        np.testing.assert_array_equal(got, want, err_msg=f"scale {s}")
+        hit_inf += int(((want & 0x7FFF) == 0x7F80).sum())
+        hit_top += int(((want & 0x7FFF) == 0x7F7F).sum())
+    assert hit_inf >= 10 and hit_top >= 4  # both sides of the overflow midpoint are exercised
+    # quotients spread over the last binade, drawn so that many land within 1 % of FLT_MAX
+    rng = np.random.default_rng(13)
+    s = np.float32(0.9921875)  # 1 - 2^-7: exact, so the fp32 quotients stay distinct
+    mant = rng.integers(0x7F7000, 0x7F8000, 4000, dtype=np.uint32)
+    bits = (mant >> 8).astype(np.uint16) | (rng.integers(0, 2, 4000, dtype=np.uint16) << 15)
+    x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float32)
+    want = (x / torch.tensor(float(s), dtype=torch.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.encode_kv("bf16", float(s), int(b)) for b in bits], dtype=np.uint16)
+    np.testing.assert_array_equal(got, want)
+    assert ((want & 0x7FFF) == 0x7F80).sum() > 100
+
+
+def test_encode_bf16_infinities_and_nan():
+    """+-inf stay +-inf (torch's cast agrees); every NaN becomes the canonical quiet NaN 0x7FC0
+    (the reading taken for the append: torch's CPU cast gives another NaN code, so only its
+    NaN-ness is a library fact)."""
+    inf = float("inf")
+    for v, s, want in [(inf, 1.0, 0x7F80), (-inf, 1.0, 0xFF80), (inf, 0.01, 0x7F80), (-inf, 7.0, 0xFF80)]:
+        b = int(_bf16_bits([v])[0])
+        lib = int((torch.tensor([v]).to(torch.bfloat16).float() / s).to(torch.bfloat16).view(torch.int16)) & 0xFFFF
+        assert oracle.encode_kv("bf16", s, b) == want == lib
+    for nan_bits in (0x7FC0, 0xFFC0, 0x7F81, 0xFF81, 0x7FFF, 0xFFFF, 0x7FA5):
+        got = oracle.encode_kv("bf16", 0.3, nan_bits)
+        assert got == 0x7FC0
+        assert math.isnan(oracle.bf16_to_double(got))
+    # finite / scale overflowing fp32 itself: the quotient is inf
+    assert oracle.encode_kv("bf16", 0.5, 0x7F7F) == 0x7F80 and oracle.encode_kv("bf16", 0.5, 0xFF7F) == 0xFF80
 
 
 @pytest.mark.parametrize("scale", [1.0, 0.0625, 0.3, 0.01])

@@ -184,3 +184,30 @@ def test_append_encoding_of_special_values():
     got_v = dc.v.cpu().numpy().reshape(want_v.shape)
     np.testing.assert_array_equal(got_k, want_k)
     np.testing.assert_array_equal(got_v, want_v)
+
+
+@pytest.mark.parametrize("ks,vs", [(0.997, 0.75), (1.01, 7.0), (0.5, 0.0625)])
+def test_append_bf16_special_values(ks, vs):
+    """The bf16 encoder at its corners, bit for bit with the oracle: quotients on both sides of
+    the overflow midpoint (rounded to infinity past it), +-inf, NaNs of either sign and any
+    payload (all become 0x7FC0), subnormals, signed zeros and the smallest normal."""
+    c = bcase(21, batch=1, K=16, hq=1, hkv=1, D=64, P=16, ctx=40, ks=ks, vs=vs)
+    inp = synth.make_inputs(c)
+    special = [0x7F7F, 0xFF7F, 0x7F7E, 0xFF7E, 0x7F7D, 0x7F70, 0x7F00, 0x7F80, 0xFF80, 0x7FC0, 0xFFC0, 0x7F81,
+               0xFF81, 0x7FFF, 0xFFFF, 0x7FA5, 0x0001, 0x8001, 0x0003, 0x007F, 0x8040, 0x0080, 0x8080, 0x0000,
+               0x8000, 0x3F80, 0xBF80, 0x3F81, 0x4049]
+    rng = np.random.default_rng(21)
+    top = (rng.integers(0x7F00, 0x7F80, 512, dtype=np.uint32) | (rng.integers(0, 2, 512, dtype=np.uint32) << 15))
+    bits = np.resize(np.concatenate([np.array(special, np.uint32), top]).astype(np.uint16), 16 * 64)
+    kb = bits.reshape(1, 16, 1, 64).copy()
+    vb = np.roll(bits, 29).reshape(1, 16, 1, 64).copy()
+    want_k, want_v = expected_append(inp, kb, vb)
+    assert ((want_k & 0x7FFF) == 0x7F80).any() and (want_k == 0x7FC0).any()
+    if 0.99 < ks < 1:  # quotients on both sides of the overflow midpoint
+        assert ((want_k & 0x7FFF) == 0x7F7F).any() or ((want_k & 0x7FFF) == 0x7F7E).any()
+    dc = H.upload(inp)
+    run_block(dc, kb, vb, append=True)  # outputs are NaN here (the block holds NaN and inf): only the cache counts
+    got_k = dc.k.view(torch.int16).cpu().numpy().view(np.uint16).reshape(want_k.shape)
+    got_v = dc.v.view(torch.int16).cpu().numpy().view(np.uint16).reshape(want_v.shape)
+    np.testing.assert_array_equal(got_k, want_k)
+    np.testing.assert_array_equal(got_v, want_v)

@@ -17,7 +17,6 @@ import oracle
 import synth
 from synth.configs import Case, find_case, fp8_variant
 from tests import gpu_harness as H
-from tests.test_gpu_configs import sample_pairs
 
 pytestmark = pytest.mark.gpu
 
@@ -132,13 +131,8 @@ def test_fp8_config_case(name):
     dc = H.upload(inp)
     out, lse, info = H.run(dc)
     del dc
-    pairs = sample_pairs(case)
-    ref_out, ref_lse = oracle.attention_case(inp, pairs=pairs)
-    g = case.group
-    sel = np.zeros(out.shape[:3], dtype=bool)
-    for b, h in pairs:
-        sel[b, :, h * g:(h + 1) * g] = True
-    res = H.compare(out, lse, ref_out, ref_lse, sel=sel, label=name)
+    ref_out, ref_lse = oracle.attention_case(inp)  # every row of the call
+    res = H.compare(out, lse, ref_out, ref_lse, label=name)
     print(f"[{name}] {res} units={info['units']}", flush=True)
 
 
