@@ -188,6 +188,32 @@ int blockattn_windowed_forward(blockattn_plan_t plan, const void* q, const void*
                                float* lse, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): blockattn_forward or
+ * blockattn_windowed_forward, whichever the plan's kind is, with no workspace
+ * argument. The work list and the partial softmax states go to a library-owned
+ * device array of BLOCKATTN_SCRATCH_BYTES on each GPU, laid out as a workspace and
+ * held until the process ends. The call allocates nothing: the array's address is
+ * looked up once per device (when a plan is made, or at the first call there).
+ *   plan     from blockattn_plan, with or without a workspace; its workspace_bytes
+ *            (blockattn_plan_info) must not exceed BLOCKATTN_SCRATCH_BYTES, else
+ *            BLOCKATTN_ERR_WORKSPACE_TOO_SMALL and nothing is launched
+ *   others   as for blockattn_forward (lse required for a windowed plan)
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (on concurrent streams, or graph replays
+ * running at the same time) race and give wrong results; order them. A plan whose
+ * requests have different split counts copies its work list (a few KB) from the
+ * plan's pinned host copy into the array on `stream` at each call, so such a plan
+ * must outlive every call and every replay of a graph that captured one. The
+ * array's input-error word is not reported (blockattn_input_errors reads a
+ * workspace).
+ */
+#define BLOCKATTN_SCRATCH_BYTES ((size_t)32 << 20)
+int blockattn_forward_scratch(blockattn_plan_t plan, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* page_table, const int32_t* seq_lens, void* out, float* lse,
+                              void* stream);
+
+/*
  * Block attention with the block's own keys and values given as dense bf16
  * arrays, either plan kind (TensorRT-LLM PR #16150: the paged DFlash context
  * kernel fuses the dense suffix of block keys into the same softmax, and the

@@ -28,6 +28,7 @@ BLOCKATTN_ERR_PLAN_MISMATCH = 4
 BLOCKATTN_ERR_HIP = 5
 BLOCKATTN_KV_BF16 = 0
 BLOCKATTN_KV_FP8_E4M3 = 1
+BLOCKATTN_SCRATCH_BYTES = 32 << 20
 BLOCKATTN_INPUT_BAD_LENGTH = 1
 BLOCKATTN_INPUT_BAD_PAGE = 2
 
@@ -37,6 +38,7 @@ EXPORTED = (
     "blockattn_forward",
     "blockattn_windowed_forward",
     "blockattn_forward_block",
+    "blockattn_forward_scratch",
     "blockattn_merge",
     "blockattn_plan_info",
     "blockattn_plan_set_profile_events",
@@ -116,6 +118,7 @@ def load_library():
     lib.blockattn_forward.argtypes = fwd
     lib.blockattn_windowed_forward.argtypes = fwd
     lib.blockattn_forward_block.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp]
+    lib.blockattn_forward_scratch.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.blockattn_merge.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp, vp, vp, vp, vp]
     lib.blockattn_plan_info.argtypes = [vp, ctypes.POINTER(blockattn_plan_info_t)]
     lib.blockattn_plan_set_profile_events.argtypes = [vp, vp, vp]
@@ -125,7 +128,7 @@ def load_library():
     lib.blockattn_plan_destroy.restype = None
     lib.blockattn_last_error.restype = ctypes.c_char_p
     for name in ("blockattn_workspace_size", "blockattn_plan", "blockattn_forward", "blockattn_windowed_forward",
-                 "blockattn_forward_block", "blockattn_merge", "blockattn_plan_info",
+                 "blockattn_forward_block", "blockattn_forward_scratch", "blockattn_merge", "blockattn_plan_info",
                  "blockattn_plan_set_profile_events", "blockattn_input_errors", "blockattn_stream_read"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -311,6 +314,16 @@ def blockattn_windowed_forward(plan: Plan, q, k_cache, v_cache, page_table, seq_
     """Non-causal windowed block attention: causal windowed decode + future-key merge (launch only)."""
     _forward("blockattn_windowed_forward", plan, q, k_cache, v_cache, page_table, seq_lens, workspace, out, lse,
              stream)
+
+
+def blockattn_forward_scratch(plan: Plan, q, k_cache, v_cache, page_table, seq_lens, out, lse=None, stream=None):
+    """Either form (the plan's kind) with no workspace: the library's per-GPU scratch array holds the
+    work list and partials (for callers that cannot allocate; overlapping calls on one GPU race)."""
+    _check_buffers(plan, q, k_cache, v_cache, page_table, seq_lens, out, lse)
+    vp = ctypes.c_void_p
+    _check(load_library().blockattn_forward_scratch(
+        vp(plan.handle), vp(_ptr(q)), vp(_ptr(k_cache)), vp(_ptr(v_cache)), vp(_ptr(page_table)), vp(_ptr(seq_lens)),
+        vp(_ptr(out)), vp(_ptr(lse)), vp(_stream(stream))))
 
 
 def blockattn_forward_block(plan: Plan, q, k_block, v_block, k_cache, v_cache, page_table, seq_lens, workspace, out,

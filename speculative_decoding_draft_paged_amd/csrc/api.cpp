@@ -72,6 +72,7 @@ struct blockattn_plan_s {
     hipEvent_t copy_done = nullptr;    // recorded after the head's upload on upload_stream
     hipStream_t upload_stream = nullptr;
     bool upload_seen_done = false;     // copy_done has been observed complete: no stream needs to wait on it
+    hipEvent_t scratch_copy_done = nullptr;  // recorded after each copy of the stage into the scratch array
     hipEvent_t prof_before = nullptr, prof_after = nullptr;
 };
 
@@ -318,9 +319,10 @@ hipError_t order_after_upload(blockattn_plan_t plan, hipStream_t st) {
     return hipStreamWaitEvent(st, plan->copy_done, 0);
 }
 
+// ws: the plan's workspace, or (from_scratch) the library's device scratch array, laid out the same.
 int run_forward(blockattn_plan_t plan, const void* q, const void* k, const void* v, const int32_t* pt,
                 const int32_t* lens, void* ws, void* out, float* lse, void* stream, const void* k_block = nullptr,
-                const void* v_block = nullptr, int append = 0) {
+                const void* v_block = nullptr, int append = 0, bool from_scratch = false) {
     const blockattn_params& p = plan->prm;
     char* base = static_cast<char*>(ws);
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -365,7 +367,7 @@ int run_forward(blockattn_plan_t plan, const void* q, const void* k, const void*
     ka.block_scale_log2 = (float)((double)p.sm_scale * 1.4426950408889634);
     ka.block_p_mul = 1.0f / p.v_scale;
 
-    hipError_t e = order_after_upload(plan, st);
+    hipError_t e = from_scratch ? hipSuccess : order_after_upload(plan, st);
     if (e != hipSuccess) return fail(BLOCKATTN_ERR_HIP, std::string("ordering after the work-list upload: ") + hipGetErrorString(e));
     if (plan->prof_before) e = hipEventRecord(plan->prof_before, st);
     if (e == hipSuccess) e = launch_attention(plan->shape, plan->kind == 1, plan->units, ka, st);
@@ -405,24 +407,40 @@ int blockattn_plan(const blockattn_params* params, const int32_t* seq_lens_host,
         delete pl;
         return rc;
     }
-    if (workspace) {
-        if (workspace_bytes < pl->lay.total) {
-            char buf[200];
-            snprintf(buf, sizeof buf, "workspace has %zu bytes but this plan needs %zu (blockattn_workspace_size)",
-                     workspace_bytes, pl->lay.total);
-            delete pl;
-            return fail(BLOCKATTN_ERR_WORKSPACE_TOO_SMALL, buf);
-        }
-        const size_t head = pl->lay.m;  // work list, pair table and the cleared input-error word
-        hipError_t e = hipHostMalloc(&pl->stage, head + kReadback, hipHostMallocDefault);
-        if (e != hipSuccess) {
+    if (workspace && workspace_bytes < pl->lay.total) {
+        char buf[200];
+        snprintf(buf, sizeof buf, "workspace has %zu bytes but this plan needs %zu (blockattn_workspace_size)",
+                 workspace_bytes, pl->lay.total);
+        delete pl;
+        return fail(BLOCKATTN_ERR_WORKSPACE_TOO_SMALL, buf);
+    }
+    // The head (work list, pair table and the cleared input-error word), staged in pinned host
+    // memory: the workspace's upload copies it now, blockattn_forward_scratch at each call. A
+    // host-only plan made where no GPU is visible keeps no stage.
+    const size_t head = pl->lay.m;
+    hipError_t e = hipHostMalloc(&pl->stage, head + kReadback, hipHostMallocDefault);
+    if (e != hipSuccess) {
+        pl->stage = nullptr;
+        if (workspace) {
             delete pl;
             return fail(BLOCKATTN_ERR_HIP, std::string("hipHostMalloc: ") + hipGetErrorString(e));
         }
+        (void)hipGetLastError();
+    } else {
         std::memset(pl->stage, 0, head);
         std::memcpy(static_cast<char*>(pl->stage) + pl->lay.work, pl->work.data(), pl->work.size() * sizeof(WorkItem));
         std::memcpy(static_cast<char*>(pl->stage) + pl->lay.pairs, pl->pair_table.data(),
                     pl->pair_table.size() * sizeof(int32_t));
+        // Set-up for blockattn_forward_scratch: the current device's scratch address, looked
+        // up once per device.
+        void* scratch = nullptr;
+        if (scratch_address(&scratch) != hipSuccess) (void)hipGetLastError();
+        if (hipEventCreateWithFlags(&pl->scratch_copy_done, hipEventDisableTiming) != hipSuccess) {
+            pl->scratch_copy_done = nullptr;
+            (void)hipGetLastError();
+        }
+    }
+    if (workspace) {
         hipStream_t st = static_cast<hipStream_t>(stream);
         e = hipMemcpyAsync(workspace, pl->stage, head, hipMemcpyHostToDevice, st);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&pl->copy_done, hipEventDisableTiming);
@@ -473,6 +491,42 @@ int blockattn_forward_block(blockattn_plan_t plan, const void* q, const void* k_
     if (rc) return rc;
     return run_forward(plan, q, k_cache, v_cache, page_table, seq_lens, workspace, out, lse, stream, k_block, v_block,
                        append);
+}
+
+int blockattn_forward_scratch(blockattn_plan_t plan, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* page_table, const int32_t* seq_lens, void* out, float* lse,
+                              void* stream) {
+    if (!plan) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "plan is NULL");
+    if (plan->lay.total > kScratchBytes) {
+        char buf[240];
+        snprintf(buf, sizeof buf,
+                 "this plan needs %zu bytes of work list and partials, more than the %zu-byte scratch array; "
+                 "use blockattn_forward / blockattn_windowed_forward with a workspace, or fewer splits",
+                 plan->lay.total, kScratchBytes);
+        return fail(BLOCKATTN_ERR_WORKSPACE_TOO_SMALL, buf);
+    }
+    if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !out)
+        return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "q, k_cache, v_cache, page_table, seq_lens and out are required");
+    if (plan->kind == 1 && !lse)
+        return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "the windowed form returns the merged LSE: lse is required");
+    if (!plan->stage)
+        return fail(BLOCKATTN_ERR_PLAN_MISMATCH, "plan has no staged work list (it was made with no GPU visible)");
+    void* scratch = nullptr;
+    hipError_t e = scratch_address(&scratch);
+    if (e != hipSuccess) return fail(BLOCKATTN_ERR_HIP, std::string("scratch array address: ") + hipGetErrorString(e));
+    if (plan->uniform_splits == 0) {
+        // Requests with different split counts: the kernels read the work list and the
+        // pair table, so this call brings its plan's copy into the shared array first. The
+        // event lets blockattn_plan_destroy wait until the copy has read the stage.
+        if (!plan->scratch_copy_done)
+            return fail(BLOCKATTN_ERR_PLAN_MISMATCH, "plan has no event for its work-list copies; plan again");
+        hipStream_t st = static_cast<hipStream_t>(stream);
+        e = hipMemcpyAsync(scratch, plan->stage, plan->lay.m, hipMemcpyHostToDevice, st);
+        if (e == hipSuccess) e = hipEventRecord(plan->scratch_copy_done, st);
+        if (e != hipSuccess) return fail(BLOCKATTN_ERR_HIP, std::string("work-list copy: ") + hipGetErrorString(e));
+    }
+    return run_forward(plan, q, k_cache, v_cache, page_table, seq_lens, scratch, out, lse, stream, nullptr, nullptr, 0,
+                       true);
 }
 
 int blockattn_merge(int32_t parts, int64_t rows, int32_t head_dim, const void* part_out, const float* part_lse,
@@ -549,6 +603,10 @@ void blockattn_plan_destroy(blockattn_plan_t plan) {
     if (plan->copy_done) {
         (void)hipEventSynchronize(plan->copy_done);
         (void)hipEventDestroy(plan->copy_done);
+    }
+    if (plan->scratch_copy_done) {
+        (void)hipEventSynchronize(plan->scratch_copy_done);
+        (void)hipEventDestroy(plan->scratch_copy_done);
     }
     if (plan->stage) (void)hipHostFree(plan->stage);
     delete plan;

@@ -82,6 +82,13 @@ hipError_t launch_combine(int head_dim, int rows, int max_splits, const KernelAr
 // Set the calling thread's last-error text (blockattn_last_error) and return code.
 int record_error(int code, const char* msg);
 
+// Bytes of the library's device scratch array (one per GPU, held until the process ends), where
+// blockattn_forward_scratch keeps the work list and partial softmax states of callers that cannot
+// allocate. Equal to BLOCKATTN_SCRATCH_BYTES.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+// Device address of the scratch array on the current device (looked up once per device).
+hipError_t scratch_address(void** ptr);
+
 // G-way LSE merge of bf16 partial results [parts, rows, head_dim] with base-2 LSEs [parts, rows].
 hipError_t launch_merge(int head_dim, int parts, int64_t rows, const uint16_t* part_out, const float* part_lse,
                         uint16_t* out, float* lse, hipStream_t stream);

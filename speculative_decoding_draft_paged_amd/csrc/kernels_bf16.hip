@@ -3,6 +3,38 @@
 
 namespace blockattn {
 
+// Scratch for blockattn_forward_scratch (callers that cannot allocate): work list, pair table,
+// input-error word and partial softmax states, laid out as a workspace. Each GPU holds its own
+// copy at its own address; host code never passes the array's name to a kernel (on the host it
+// is only a stand-in), only the device address scratch_address looked up with that device current.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kScratchDevices];  // static storage: starts at nullptr
+}  // namespace
+
+hipError_t scratch_address(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool tracked = dev >= 0 && dev < kScratchDevices;
+    if (tracked) {
+        void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+        if (p) {
+            *ptr = p;
+            return hipSuccess;
+        }
+    }
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    if (tracked) g_scratch_ptr[dev].store(p, std::memory_order_release);
+    *ptr = p;
+    return hipSuccess;
+}
+
 size_t attention_lds_bytes(const KernelShape& s, int R) {
     (void)R;
     const int D = s.head_dim;

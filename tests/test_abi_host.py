@@ -169,6 +169,29 @@ def test_forward_refuses_plans_without_workspace_or_wrong_kind():
     plan.destroy()
 
 
+def test_scratch_forward_refuses_plans_larger_than_the_array():
+    """A plan whose work list and partials exceed the scratch array is refused before any HIP call."""
+    lib = ba.load_library()
+    # 16 requests x 2 kv heads x 1000 forced splits of 28 rows: about 115 MB of partials
+    prm = ba.make_params(batch=16, block_size=7, num_q_heads=8, num_kv_heads=2, head_dim=64, page_size=32,
+                         page_table_stride=2000, num_pages=40000, sm_scale=0.125, splits_override=1000)
+    lens = np.full(16, 40000, np.int32)
+    assert ba.blockattn_workspace_size(prm, lens) > ba.BLOCKATTN_SCRATCH_BYTES
+    plan = ba.blockattn_plan(prm, lens)
+    vp = ctypes.c_void_p
+    one = vp(0x1000)
+    rc = lib.blockattn_forward_scratch(vp(plan.handle), one, one, one, one, one, one, None, None)
+    assert rc == ba.BLOCKATTN_ERR_WORKSPACE_TOO_SMALL and "scratch" in ba.blockattn_last_error()
+    rc = lib.blockattn_forward_scratch(None, one, one, one, one, one, one, None, None)
+    assert rc == ba.BLOCKATTN_ERR_INVALID_ARGUMENT
+    plan.destroy()
+    # a windowed plan that fits still needs its lse
+    ok = ba.blockattn_plan(params(window_left=64), [100, 100])
+    rc = lib.blockattn_forward_scratch(vp(ok.handle), one, one, one, one, one, one, None, None)
+    assert rc == ba.BLOCKATTN_ERR_INVALID_ARGUMENT and "lse" in ba.blockattn_last_error()
+    ok.destroy()
+
+
 def test_forward_block_checks_its_own_arguments_first():
     lib = ba.load_library()
     vp = ctypes.c_void_p
