@@ -130,7 +130,48 @@ def load_traffic(case_name: str, per_launch_bytes: int):
     return rec.get("hbm_bytes_per_launch")
 
 
-def run_case(case, steps, warmup, threads, graph=True, splits=0, waves=0, block="cache", replays=10):
+TRACE_PHASES = ("entry", "length", "pages", "loop", "epilogue", "stored")
+
+
+def phase_stats(calls):
+    """Per-unit phase timestamps (100 MHz ticks, [units, 8] per traced call) as a timeline in us.
+
+    For each call, times are taken from the earliest unit entry; each statistic is the median
+    over units (and the max for the ends), then the median over calls."""
+    import numpy as np
+
+    per_call = []
+    for tr in calls:
+        tr = tr.astype(np.int64)
+        e, ln, pg, lp, ep, st = (tr[:, k] for k in range(6))
+        ok = (e > 0) & (ln > 0) & (pg > 0) & (lp > 0) & (st > 0)
+        e, ln, pg, lp, ep, st = e[ok], ln[ok], pg[ok], lp[ok], ep[ok], st[ok]
+        t0 = e.min()
+        us = lambda x: x * 0.01  # 10 ns per tick
+        has_ep = bool((ep > 0).all())
+        row = {
+            "units_traced": int(ok.sum()),
+            "entry_spread_us": us(e.max() - t0),
+            "entry_median_us": us(np.median(e - t0)),
+            "length_latency_us": us(np.median(ln - e)),
+            "pages_latency_us": us(np.median(pg - ln)),
+            "loop_us": us(np.median(lp - pg)),
+            "slowest_group_wait_us": us(np.median(ep - lp)) if has_ep else 0.0,
+            "epilogue_us": us(np.median(st - (ep if has_ep else lp))),
+            "unit_end_median_us": us(np.median(st - t0)),
+            "unit_end_max_us": us(st.max() - t0),
+            "unit_end_p10_us": us(np.percentile(st - t0, 10)),
+            "unit_end_p90_us": us(np.percentile(st - t0, 90)),
+        }
+        per_call.append(row)
+    out = {k: (round(float(np.median([r[k] for r in per_call])), 3) if k != "units_traced" else per_call[0][k])
+           for k in per_call[0]}
+    out["calls"] = len(per_call)
+    return out
+
+
+def run_case(case, steps, warmup, threads, graph=True, splits=0, waves=0, block="cache", replays=10,
+             trace_calls=0, combine="auto"):
     import numpy as np
     import torch
 
@@ -168,7 +209,8 @@ def run_case(case, steps, warmup, threads, graph=True, splits=0, waves=0, block=
                          num_kv_heads=case.num_kv_heads, head_dim=case.head_dim, page_size=case.page_size,
                          page_table_stride=inp.page_table.shape[1], num_pages=inp.num_pages, sm_scale=case.scale,
                          window_left=case.window_left, window_right=case.window_right, splits_override=splits,
-                         waves_override=waves, kv_dtype=case.kv_dtype, k_scale=case.k_scale, v_scale=case.v_scale)
+                         waves_override=waves, kv_dtype=case.kv_dtype, k_scale=case.k_scale, v_scale=case.v_scale,
+                         combine=combine)
     nbytes = ba.blockattn_workspace_size(prm, inp.seq_lens)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     plan = ba.blockattn_plan(prm, inp.seq_lens, ws, nbytes)
@@ -245,6 +287,26 @@ def run_case(case, steps, warmup, threads, graph=True, splits=0, waves=0, block=
     timing = "eager"
     hip.destroy(before + after + [ga, gb])
     info = plan.info()
+    phases = None
+    if trace_calls > 0:
+        # Traced eager calls: per-unit phase timestamps, and the attention kernel's event time of
+        # the same calls (the trace's waits make them a little slower than untraced calls).
+        tr = torch.zeros(info["units"] * 8, dtype=torch.int64, device=dev)
+        ba.blockattn_plan_set_phase_trace(plan, tr)
+        tb, ta = hip.create(trace_calls), hip.create(trace_calls)
+        calls = []
+        for i in range(trace_calls):
+            tr.zero_()
+            ba.blockattn_plan_set_profile_events(plan, tb[i], ta[i])
+            step(i)
+            torch.cuda.synchronize()
+            calls.append(tr.view(info["units"], 8).cpu().numpy())
+        ba.blockattn_plan_set_profile_events(plan, None, None)
+        ba.blockattn_plan_set_phase_trace(plan, None)
+        phases = phase_stats(calls)
+        phases["traced_kernel_event_us"] = round(float(np.median([hip.elapsed_ms(tb[i], ta[i]) for i in
+                                                                   range(trace_calls)])) * 1e3, 2)
+        hip.destroy(tb + ta)
     res = {
         "case": case.name,
         "kv_bytes": kv_bytes(case, inp.seq_lens, block),
@@ -264,6 +326,8 @@ def run_case(case, steps, warmup, threads, graph=True, splits=0, waves=0, block=
         "waves_per_unit": info["waves_per_unit"],
         "shared_tiles": info["shared_tiles"],
         "combine_launch": info["combine_launch"],
+        "fused_combine": info["fused_combine"],
+        "phases": phases,
     }
     plan.destroy()
     return res, inp, out, blocks
@@ -275,7 +339,7 @@ READ_BYTES = 2 << 30  # the read-only streaming reference reads 2 GiB per launch
 def read_reference(reps=20):
     """The read-only streaming reference: blockattn_stream_read over 2 GiB (every byte read once with
     the attention kernels' 16-byte non-temporal loads), median of `reps` launches timed with HIP
-    events, at three launch widths; the best median is the box's achievable HBM read rate."""
+    events, at five launch widths; the best median is the box's achievable HBM read rate."""
     import numpy as np
     import torch
 
@@ -287,7 +351,7 @@ def read_reference(reps=20):
     evs = hip.create(2 * reps)
     stream = torch.cuda.current_stream().cuda_stream
     best = None
-    for wg in (1024, 2048, 4096):
+    for wg in (256, 512, 1024, 2048, 4096):
         for _ in range(3):
             ba.blockattn_stream_read(src, acc, wg)
         torch.cuda.synchronize()
@@ -298,7 +362,8 @@ def read_reference(reps=20):
         torch.cuda.synchronize()
         us = float(np.median([hip.elapsed_ms(evs[2 * r], evs[2 * r + 1]) for r in range(reps)])) * 1e3
         if best is None or us < best["us"]:
-            best = {"kernel": "blockattn_stream_read, 2 GiB read once (16-byte non-temporal loads)", "workgroups": wg,
+            best = {"kernel": "blockattn_stream_read, 2 GiB read once (16-byte non-temporal loads, a contiguous "
+                              "range per workgroup)", "workgroups": wg,
                     "us": round(us, 1), "gbs": round(READ_BYTES / (us * 1e-6) / 1e9, 1), "reps": reps}
     hip.destroy(evs)
     best["frac_of_peak"] = round(best["gbs"] / HBM_PEAK_GBS, 4)
@@ -450,6 +515,43 @@ def cpu_baseline(case, inp, gpu_out, kv_total, budget_s, blocks=None):
     }
 
 
+def write_phase_summary(name, row, args):
+    """profiles/phases_<case>.md: the traced phase timeline of the attention kernel for one case."""
+    ph = row["phases"]
+    cmd = "python bench.py " + " ".join(sys.argv[1:])
+    lines = [
+        f"# Phase timeline of the attention kernel: {name}",
+        "",
+        f"Command: `{cmd}`",
+        "",
+        f"Kernel source digest {kernel_source_digest()}. One traced eager call = one `blockattn_forward` for the "
+        f"whole batch; {ph['calls']} traced calls, {ph['units_traced']} work units each; every figure is the "
+        "median over units (ends also as p10 / p90 / max), then the median over calls. Times in us from the "
+        "earliest unit's first instruction, in the GPU's 100 MHz constant clock. Each phase ends when the "
+        "unit's memory operations in flight have completed, so traced calls run a little slower than untraced ones.",
+        "",
+        "| phase | us |",
+        "|---|---|",
+        f"| untraced call (graph replays, median) | {row['us_per_call']} |",
+        f"| untraced attention kernel (HIP events) | {row['kernel_us']} |",
+        f"| traced attention kernel (HIP events) | {ph['traced_kernel_event_us']} |",
+        f"| last unit entry after the first (dispatch spread) | {ph['entry_spread_us']} |",
+        f"| sequence length loaded, after entry | {ph['length_latency_us']} |",
+        f"| first page ids staged, after the length | {ph['pages_latency_us']} |",
+        f"| token group 0's tile loop | {ph['loop_us']} |",
+        f"| wait for the unit's slowest token group | {ph['slowest_group_wait_us']} |",
+        f"| epilogue (merge of token groups, stores complete) | {ph['epilogue_us']} |",
+        f"| unit end: median / p10 / p90 / max | {ph['unit_end_median_us']} / {ph['unit_end_p10_us']} / "
+        f"{ph['unit_end_p90_us']} / {ph['unit_end_max_us']} |",
+        "",
+        f"Per call: {row['kv_bytes']} bytes of KV, {row['units']} units, at most {row['max_splits']} splits per "
+        f"(request, kv head); combine launch: {'yes' if row['combine_launch'] else 'no'}.",
+        "",
+    ]
+    with open(os.path.join(ROOT, args.summary_dir, f"phases_{name}.md"), "w") as f:
+        f.write("\n".join(lines))
+
+
 def case_list(spec):
     """Names of the per-case array: the ten 128K-context cases by default."""
     from synth.configs import all_cases
@@ -477,7 +579,8 @@ def per_case_array(names, head_case, head_res, args, threads):
         if name == head_case.name and args.block == "cache" and not args.splits and not args.waves:
             r = head_res
         else:
-            r, _, _, _ = run_case(c, args.case_steps, 3, threads, graph=not args.eager, replays=args.replays)
+            r, _, _, _ = run_case(c, args.case_steps, 3, threads, graph=not args.eager, replays=args.replays,
+                                  trace_calls=args.phase_trace, combine=args.combine)
             torch.cuda.empty_cache()
         gbs = r["kv_bytes"] / (r["step_ms"] * 1e-3) / 1e9
         kgbs = r["kv_bytes"] / (r["partial_ms"] * 1e-3) / 1e9
@@ -486,7 +589,12 @@ def per_case_array(names, head_case, head_res, args, threads):
                "kernel_us": round(r["partial_ms"] * 1e3, 2), "kernel_frac": round(kgbs / HBM_PEAK_GBS, 4),
                "us_min": round(r["step_ms_min"] * 1e3, 2), "us_max": round(r["step_ms_max"] * 1e3, 2),
                "steps": args.case_steps if r is not head_res else args.steps, "replays": r["replays"],
-               "units": r["units"], "max_splits": r["max_splits"], "combine_launch": r["combine_launch"]}
+               "units": r["units"], "max_splits": r["max_splits"], "combine_launch": r["combine_launch"],
+               "fused_combine": r["fused_combine"]}
+        if r.get("phases"):
+            row["phases"] = r["phases"]
+            if args.phase_summary:
+                write_phase_summary(name, row, args)
         rows.append(row)
         log(f"[case] {name:16s} {row['us_per_call']:9.2f} us/call  {gbs:7.0f} GB/s  ({100 * row['frac']:5.1f} % of 8 TB/s)"
             f"  kernel {row['kernel_us']:9.2f} us ({100 * row['kernel_frac']:5.1f} %)  units {row['units']}")
@@ -505,6 +613,9 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--splits", type=int, default=0, help="force the split count per (request, kv head)")
     ap.add_argument("--waves", type=int, default=0, help="force the tile-streaming waves per workgroup")
+    ap.add_argument("--combine", choices=("auto", "kernel", "last_arriver"), default="auto",
+                    help="split combine: the plan's choice, the combine kernel, or the last split inside the "
+                         "attention kernel")
     ap.add_argument("--block", choices=("cache", "dense", "append"), default="cache",
                     help="where the block's keys and values come from: the cache (default), dense arrays, or "
                          "dense arrays also appended into the cache in the same call")
@@ -515,6 +626,12 @@ def main():
                          "'none', or a comma-separated list of case names")
     ap.add_argument("--case-steps", type=int, default=20, help="calls per timed run for the per-case array")
     ap.add_argument("--no-read-reference", action="store_true", help="skip the read-only 2 GiB streaming reference")
+    ap.add_argument("--phase-trace", type=int, default=0, metavar="CALLS",
+                    help="also trace CALLS eager calls of each timed case (per-unit phase timestamps) and report "
+                         "the phase timeline; with --phase-summary, write it to profiles/phases_<case>.md")
+    ap.add_argument("--phase-summary", action="store_true",
+                    help="write the phase timelines to <summary-dir>/phases_<case>.md (needs --phase-trace)")
+    ap.add_argument("--summary-dir", default="profiles", help="folder (under the repository) for --phase-summary")
     ap.add_argument("--copy-reference", action="store_true",
                     help="also time a plain 1 GiB elementwise copy (achievable HBM rate; PMC calibration kernel)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH", "WRITE"),
@@ -554,7 +671,8 @@ def main():
 
     case = find_case(args.case)
     res, inp, out, blocks = run_case(case, args.steps, args.warmup, threads, graph=not args.eager,
-                                     splits=args.splits, waves=args.waves, block=args.block, replays=args.replays)
+                                     splits=args.splits, waves=args.waves, block=args.block, replays=args.replays,
+                                     trace_calls=args.phase_trace, combine=args.combine)
     kvb = res["kv_bytes"]
     value = kvb / (res["step_ms"] * 1e-3) / 1e9
     achieved = kvb / (res["partial_ms"] * 1e-3) / 1e9
@@ -569,7 +687,8 @@ def main():
             if case.kv_dtype != "bf16":
                 c = fp8_variant(c, case.k_scale, case.v_scale)
             r, _, _, _ = run_case(c, max(10, args.steps // 2), 3, threads, graph=not args.eager,
-                                  splits=args.splits, waves=args.waves, block=args.block, replays=args.replays)
+                                  splits=args.splits, waves=args.waves, block=args.block, replays=args.replays,
+                                  combine=args.combine)
             r["gbs"] = r["kv_bytes"] / (r["step_ms"] * 1e-3) / 1e9
             r["frac"] = r["gbs"] / HBM_PEAK_GBS
             r["partial_gbs"] = r["kv_bytes"] / (r["partial_ms"] * 1e-3) / 1e9

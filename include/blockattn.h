@@ -95,7 +95,19 @@ typedef struct blockattn_params {
     float k_scale;             /* finite and > 0: a stored key element stands for k_scale times its
                                   value (1 for an unscaled cache) */
     float v_scale;             /* finite: a stored value element stands for v_scale times its value */
+    int32_t combine_mode;      /* how the splits of a split request are combined (TensorRT-LLM PR #20374,
+                                  Description: the multi-CTA split-KV decode combines its splits through
+                                  counter buffers): BLOCKATTN_COMBINE_AUTO (0) lets the plan choose (the
+                                  combine kernel, the faster of the two wherever measured on MI355X);
+                                  BLOCKATTN_COMBINE_KERNEL (1) launches a separate combine kernel;
+                                  BLOCKATTN_COMBINE_LAST_ARRIVER (2) has the last split of each
+                                  (request, kv head) to finish combine them inside the attention kernel,
+                                  found by a per-(request, kv head) arrival counter in the workspace
+                                  (refused with BLOCKATTN_ERR_UNSUPPORTED when the split statistics do not
+                                  fit the kernel's LDS) */
 } blockattn_params;
+
+enum { BLOCKATTN_COMBINE_AUTO = 0, BLOCKATTN_COMBINE_KERNEL = 1, BLOCKATTN_COMBINE_LAST_ARRIVER = 2 };
 
 enum { BLOCKATTN_KV_BF16 = 0, BLOCKATTN_KV_FP8_E4M3 = 1 };
 
@@ -118,13 +130,16 @@ typedef struct blockattn_plan_info {
     int32_t row_groups;        /* work units per (request, kv head, split): 1 up to 128 query rows per
                                   kv head; above that the rows are split into this many groups of at
                                   most 128, each reading the kv head's keys */
+    int32_t fused_combine;     /* 1: split requests are combined inside the attention kernel by the last
+                                  split to finish (no combine launch); 0: by the combine kernel, if any */
     size_t workspace_bytes;    /* bytes the plan needs */
 } blockattn_plan_info_t;
 
 /*
  * Exact workspace bytes needed for these parameters and host lengths: the
- * split-KV work list, the per-(request, kv head) table, the input-error word and
- * the fp32 partial softmax states (acc, m, l) of every work unit. The size is
+ * split-KV work list, the per-(request, kv head) table and arrival counters, the
+ * input-error word and the fp32 partial softmax states (acc, m, l) of every work
+ * unit. The size is
  * computed from the same plan a forward runs, so the softmax statistics can never
  * outgrow their carve (TensorRT-LLM PR #21130, Description item 3: the workspace
  * must hold the stats, and a launch is refused when it is too small).
@@ -267,6 +282,20 @@ int blockattn_merge(int32_t parts, int64_t rows, int32_t head_dim, const void* p
  */
 int blockattn_plan_info(blockattn_plan_t plan, blockattn_plan_info_t* info);
 
+/*
+ * Profiling aid: per-phase timestamps of the split-KV partial kernel. With a
+ * device buffer of at least units * 8 uint64 (units from blockattn_plan_info),
+ * every later forward on this plan has each work unit (workgroup) write, after
+ * its memory operations in flight have completed, the 100 MHz constant GPU clock
+ * at: [0] kernel entry, [1] its sequence length loaded, [2] its first window of
+ * page ids staged, [3] token group 0's tile loop done, [4] all token groups done
+ * (multi-group units only), [5] its output or partial stored; [6] and [7] are
+ * unused. Entry u * 8 + k is unit u's phase k. The waits make traced calls a
+ * little slower. NULL stops tracing. Not for use during graph capture.
+ * Returns BLOCKATTN_ERR_WORKSPACE_TOO_SMALL when the buffer is too small.
+ */
+int blockattn_plan_set_phase_trace(blockattn_plan_t plan, void* trace, size_t bytes);
+
 /* Bits of the input-error word. */
 enum {
     BLOCKATTN_INPUT_BAD_LENGTH = 1, /* a device seq_lens entry was outside [K, page_table_stride * P] */
@@ -306,7 +335,7 @@ int blockattn_plan_set_profile_events(blockattn_plan_t plan, void* before, void*
  *   src         device buffer, 16-byte aligned
  *   bytes       a positive multiple of 16
  *   result      device uint32; the caller zeroes it first if it wants the fold's value
- *   workgroups  256-thread workgroups to launch (0: 2048, eight per compute unit)
+ *   workgroups  256-thread workgroups, each reading one contiguous range (0: 1024)
  *   stream      hipStream_t. Launch only: no allocation, no host synchronisation.
  */
 int blockattn_stream_read(const void* src, size_t bytes, uint32_t* result, int32_t workgroups, void* stream);

@@ -28,6 +28,10 @@ BLOCKATTN_ERR_PLAN_MISMATCH = 4
 BLOCKATTN_ERR_HIP = 5
 BLOCKATTN_KV_BF16 = 0
 BLOCKATTN_KV_FP8_E4M3 = 1
+BLOCKATTN_COMBINE_AUTO = 0
+BLOCKATTN_COMBINE_KERNEL = 1
+BLOCKATTN_COMBINE_LAST_ARRIVER = 2
+COMBINE_MODES = {"auto": 0, "kernel": 1, "last_arriver": 2}
 BLOCKATTN_SCRATCH_BYTES = 32 << 20
 BLOCKATTN_INPUT_BAD_LENGTH = 1
 BLOCKATTN_INPUT_BAD_PAGE = 2
@@ -42,6 +46,7 @@ EXPORTED = (
     "blockattn_merge",
     "blockattn_plan_info",
     "blockattn_plan_set_profile_events",
+    "blockattn_plan_set_phase_trace",
     "blockattn_input_errors",
     "blockattn_stream_read",
     "blockattn_plan_destroy",
@@ -67,6 +72,7 @@ class blockattn_params(ctypes.Structure):
         ("kv_dtype", ctypes.c_int32),
         ("k_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float),
+        ("combine_mode", ctypes.c_int32),
     ]
 
 
@@ -83,6 +89,7 @@ class blockattn_plan_info_t(ctypes.Structure):
         ("combine_launch", ctypes.c_int32),
         ("shared_tiles", ctypes.c_int32),
         ("row_groups", ctypes.c_int32),
+        ("fused_combine", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -123,13 +130,15 @@ def load_library():
     lib.blockattn_plan_info.argtypes = [vp, ctypes.POINTER(blockattn_plan_info_t)]
     lib.blockattn_plan_set_profile_events.argtypes = [vp, vp, vp]
     lib.blockattn_input_errors.argtypes = [vp, vp, vp, i32p]
+    lib.blockattn_plan_set_phase_trace.argtypes = [vp, vp, ctypes.c_size_t]
     lib.blockattn_stream_read.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_int32, vp]
     lib.blockattn_plan_destroy.argtypes = [vp]
     lib.blockattn_plan_destroy.restype = None
     lib.blockattn_last_error.restype = ctypes.c_char_p
     for name in ("blockattn_workspace_size", "blockattn_plan", "blockattn_forward", "blockattn_windowed_forward",
                  "blockattn_forward_block", "blockattn_forward_scratch", "blockattn_merge", "blockattn_plan_info",
-                 "blockattn_plan_set_profile_events", "blockattn_input_errors", "blockattn_stream_read"):
+                 "blockattn_plan_set_profile_events", "blockattn_plan_set_phase_trace", "blockattn_input_errors",
+                 "blockattn_stream_read"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -149,11 +158,12 @@ KV_DTYPES = {"bf16": BLOCKATTN_KV_BF16, "fp8_e4m3": BLOCKATTN_KV_FP8_E4M3}
 
 def make_params(*, batch, block_size, num_q_heads, num_kv_heads, head_dim, page_size, page_table_stride, num_pages,
                 sm_scale, window_left=-1, window_right=-1, splits_override=0, waves_override=0, kv_dtype="bf16",
-                k_scale=1.0, v_scale=1.0) -> blockattn_params:
+                k_scale=1.0, v_scale=1.0, combine="auto") -> blockattn_params:
     code = KV_DTYPES[kv_dtype] if isinstance(kv_dtype, str) else int(kv_dtype)
+    mode = COMBINE_MODES[combine] if isinstance(combine, str) else int(combine)
     return blockattn_params(batch, block_size, num_q_heads, num_kv_heads, head_dim, page_size, page_table_stride,
                             num_pages, window_left, window_right, float(sm_scale), splits_override, waves_override,
-                            code, float(k_scale), float(v_scale))
+                            code, float(k_scale), float(v_scale), mode)
 
 
 def _host_lens(seq_lens_host):
@@ -242,6 +252,17 @@ def blockattn_plan_set_profile_events(plan: Plan, before, after):
     """Record raw hipEvent_t handles (ints) around the partial kernel of later forwards; None stops."""
     _check(load_library().blockattn_plan_set_profile_events(ctypes.c_void_p(plan.handle), ctypes.c_void_p(before),
                                                             ctypes.c_void_p(after)))
+
+
+def blockattn_plan_set_phase_trace(plan: Plan, trace):
+    """Per-unit phase timestamps of later forwards into `trace` (int64 device tensor of units * 8); None stops."""
+    if trace is None:
+        _check(load_library().blockattn_plan_set_phase_trace(ctypes.c_void_p(plan.handle), None, 0))
+        return
+    if not trace.is_cuda or not trace.is_contiguous():
+        raise ValueError("trace must be a contiguous device tensor")
+    _check(load_library().blockattn_plan_set_phase_trace(ctypes.c_void_p(plan.handle), ctypes.c_void_p(_ptr(trace)),
+                                                         trace.numel() * trace.element_size()))
 
 
 def blockattn_input_errors(plan: Plan, workspace, stream=None) -> int:

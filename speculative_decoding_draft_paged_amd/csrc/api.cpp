@@ -47,8 +47,9 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Workspace sections, each 256-byte aligned. The head (work list, pair table and the
 // input-error word) is what the plan uploads; the partials follow it.
 struct Layout {
-    size_t work = 0, pairs = 0, err = 0, m = 0, l = 0, acc = 0, total = 0;
+    size_t work = 0, pairs = 0, cnt = 0, err = 0, m = 0, l = 0, acc = 0, total = 0;
 };
+
 
 }  // namespace
 
@@ -61,6 +62,7 @@ struct blockattn_plan_s {
     int R_all = 1, G = 1;      // query rows per kv head, split into G row groups of R
     KernelShape shape{};
     bool merge_active = false;
+    bool fused = false;  // split pairs combined in the attention kernel by their last unit
     int units = 0, max_splits = 0;
     int uniform_splits = 0;  // > 0 when every (request, kv head) has this split count
     std::vector<WorkItem> work;
@@ -74,6 +76,7 @@ struct blockattn_plan_s {
     bool upload_seen_done = false;     // copy_done has been observed complete: no stream needs to wait on it
     hipEvent_t scratch_copy_done = nullptr;  // recorded after each copy of the stage into the scratch array
     hipEvent_t prof_before = nullptr, prof_after = nullptr;
+    uint64_t* trace = nullptr;  // per-unit phase timestamps (profiling aid), or NULL
 };
 
 namespace {
@@ -118,6 +121,9 @@ int validate(const blockattn_params* p, const int32_t* lens) {
     if (p->splits_override < 0) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "splits_override must be >= 0");
     if (p->waves_override < 0 || p->waves_override > kMaxWaves)
         return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "waves_override must be in [0, 8]");
+    if (p->combine_mode < BLOCKATTN_COMBINE_AUTO || p->combine_mode > BLOCKATTN_COMBINE_LAST_ARRIVER)
+        return fail(BLOCKATTN_ERR_INVALID_ARGUMENT,
+                    "combine_mode must be BLOCKATTN_COMBINE_AUTO (0), _KERNEL (1) or _LAST_ARRIVER (2)");
     const long max_keys = (long)p->page_table_stride * p->page_size;
     if (max_keys > (1L << 30))
         return fail(BLOCKATTN_ERR_UNSUPPORTED, "page_table_stride * page_size must be <= 2^30 keys");
@@ -271,10 +277,28 @@ int build_plan(const blockattn_params* p, const int32_t* lens, blockattn_plan_s*
     for (size_t pr = 0; pr < (size_t)B * H; ++pr)
         if (pl->pair_table[2 * pr + 1] != pl->max_splits) pl->uniform_splits = 0;
 
+    // Split combine: by the combine kernel, or in the attention kernel by each pair's last unit.
+    // The automatic choice is the combine kernel: on MI355X it measured faster at every batch of
+    // the Kimi-style rank at 128K (B = 1 ... 16), because the last arriver alone reads all of its
+    // pair's partials through device-scope loads while the combine kernel spreads them over
+    // many workgroups.
+    pl->fused = false;
+    if (pl->max_splits > 1 && p->combine_mode == BLOCKATTN_COMBINE_LAST_ARRIVER) {
+        if (last_arriver_lds_floats(pl->max_splits, pl->R) * sizeof(float) > pl->shape.lds_bytes) {
+            char buf[200];
+            snprintf(buf, sizeof buf,
+                     "the in-kernel combine of %d splits of %d rows needs more LDS than the kernel has; use "
+                     "BLOCKATTN_COMBINE_KERNEL or fewer splits", pl->max_splits, pl->R);
+            return fail(BLOCKATTN_ERR_UNSUPPORTED, buf);
+        }
+        pl->fused = true;
+    }
+
     Layout& L = pl->lay;
     L.work = 0;
     L.pairs = align_up(L.work + pl->work.size() * sizeof(WorkItem), 256);
-    L.err = align_up(L.pairs + pl->pair_table.size() * sizeof(int32_t), 256);
+    L.cnt = align_up(L.pairs + pl->pair_table.size() * sizeof(int32_t), 256);
+    L.err = align_up(L.cnt + (size_t)B * H * sizeof(uint32_t), 256);
     L.m = align_up(L.err + sizeof(uint32_t), 256);
     L.l = align_up(L.m + (size_t)pl->units * pl->R * sizeof(float), 256);
     L.acc = align_up(L.l + (size_t)pl->units * pl->R * sizeof(float), 256);
@@ -343,6 +367,8 @@ int run_forward(blockattn_plan_t plan, const void* q, const void* k, const void*
     ka.part_l = reinterpret_cast<float*>(base + plan->lay.l);
     ka.part_acc = reinterpret_cast<float*>(base + plan->lay.acc);
     ka.err = reinterpret_cast<uint32_t*>(base + plan->lay.err);
+    ka.counters = reinterpret_cast<uint32_t*>(base + plan->lay.cnt);
+    ka.fused_combine = plan->fused ? 1 : 0;
     ka.out = static_cast<uint16_t*>(out);
     ka.lse = lse;
     ka.K = p.block_size;
@@ -366,6 +392,7 @@ int run_forward(blockattn_plan_t plan, const void* q, const void* k, const void*
     ka.v_scale = p.v_scale;
     ka.block_scale_log2 = (float)((double)p.sm_scale * 1.4426950408889634);
     ka.block_p_mul = 1.0f / p.v_scale;
+    ka.trace = plan->trace;
 
     hipError_t e = from_scratch ? hipSuccess : order_after_upload(plan, st);
     if (e != hipSuccess) return fail(BLOCKATTN_ERR_HIP, std::string("ordering after the work-list upload: ") + hipGetErrorString(e));
@@ -373,7 +400,7 @@ int run_forward(blockattn_plan_t plan, const void* q, const void* k, const void*
     if (e == hipSuccess) e = launch_attention(plan->shape, plan->kind == 1, plan->units, ka, st);
     if (e == hipSuccess && plan->prof_after) e = hipEventRecord(plan->prof_after, st);
     if (e != hipSuccess) return fail(BLOCKATTN_ERR_HIP, std::string("attention kernel launch: ") + hipGetErrorString(e));
-    if (plan->max_splits > 1) {
+    if (plan->max_splits > 1 && !plan->fused) {
         const int rows = p.batch * p.num_kv_heads * plan->R_all;
         e = launch_combine(p.head_dim, rows, plan->max_splits, ka, st);
         if (e != hipSuccess)
@@ -414,7 +441,7 @@ int blockattn_plan(const blockattn_params* params, const int32_t* seq_lens_host,
         delete pl;
         return fail(BLOCKATTN_ERR_WORKSPACE_TOO_SMALL, buf);
     }
-    // The head (work list, pair table and the cleared input-error word), staged in pinned host
+    // The head (work list, pair table, zeroed arrival counters and input-error word), staged in pinned host
     // memory: the workspace's upload copies it now, blockattn_forward_scratch at each call. A
     // host-only plan made where no GPU is visible keeps no stage.
     const size_t head = pl->lay.m;
@@ -514,10 +541,12 @@ int blockattn_forward_scratch(blockattn_plan_t plan, const void* q, const void* 
     void* scratch = nullptr;
     hipError_t e = scratch_address(&scratch);
     if (e != hipSuccess) return fail(BLOCKATTN_ERR_HIP, std::string("scratch array address: ") + hipGetErrorString(e));
-    if (plan->uniform_splits == 0) {
-        // Requests with different split counts: the kernels read the work list and the
-        // pair table, so this call brings its plan's copy into the shared array first. The
-        // event lets blockattn_plan_destroy wait until the copy has read the stage.
+    if (plan->uniform_splits == 0 || plan->fused) {
+        // Requests with different split counts: the kernels read the work list and the pair
+        // table; an in-kernel combine: its arrival counters must start at zero, whatever an
+        // earlier call left in the array. So this call brings its plan's head (work list, pair
+        // table, zeroed counters) into the shared array first. The event lets
+        // blockattn_plan_destroy wait until the copy has read the stage.
         if (!plan->scratch_copy_done)
             return fail(BLOCKATTN_ERR_PLAN_MISMATCH, "plan has no event for its work-list copies; plan again");
         hipStream_t st = static_cast<hipStream_t>(stream);
@@ -561,7 +590,8 @@ int blockattn_plan_info(blockattn_plan_t plan, blockattn_plan_info_t* info) {
     info->token_groups = plan->shape.token_groups;
     info->row_waves = plan->shape.row_waves;
     info->uploaded = plan->uploaded ? 1 : 0;
-    info->combine_launch = plan->max_splits > 1 ? 1 : 0;
+    info->combine_launch = plan->max_splits > 1 && !plan->fused ? 1 : 0;
+    info->fused_combine = plan->fused ? 1 : 0;
     info->shared_tiles = plan->shape.shared ? 1 : 0;
     info->row_groups = plan->G;
     info->workspace_bytes = plan->lay.total;
@@ -574,6 +604,20 @@ int blockattn_plan_set_profile_events(blockattn_plan_t plan, void* before, void*
         return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "pass both profiling events or neither");
     plan->prof_before = static_cast<hipEvent_t>(before);
     plan->prof_after = static_cast<hipEvent_t>(after);
+    return BLOCKATTN_OK;
+}
+
+int blockattn_plan_set_phase_trace(blockattn_plan_t plan, void* trace, size_t bytes) {
+    if (!plan) return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "plan is NULL");
+    if (trace && bytes < (size_t)plan->units * kTracePoints * sizeof(uint64_t)) {
+        char buf[160];
+        snprintf(buf, sizeof buf, "trace buffer has %zu bytes; this plan's %d units need %zu", bytes, plan->units,
+                 (size_t)plan->units * kTracePoints * sizeof(uint64_t));
+        return fail(BLOCKATTN_ERR_WORKSPACE_TOO_SMALL, buf);
+    }
+    if (trace && (reinterpret_cast<uintptr_t>(trace) & 7u) != 0)
+        return fail(BLOCKATTN_ERR_INVALID_ARGUMENT, "trace buffer must be 8-byte aligned");
+    plan->trace = static_cast<uint64_t*>(trace);
     return BLOCKATTN_OK;
 }
 

@@ -98,6 +98,18 @@ __device__ __forceinline__ void flag_input_error(uint32_t* err, uint32_t bits) {
     __hip_atomic_fetch_or(err, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Profiling aid: when the caller gave a trace buffer, the workgroup's first lane writes the
+// constant 100 MHz clock for phase `k` of this unit, after every memory operation the wave has in
+// flight has completed (so a phase ends when its data has arrived). Off (one uniform branch) when
+// no buffer is given.
+__device__ __forceinline__ void trace_point(const KernelArgs& a, int k) {
+    if (a.trace != nullptr) {
+        __builtin_amdgcn_s_waitcnt(0);
+        const uint64_t t = __builtin_amdgcn_s_memrealtime();
+        if (threadIdx.x == 0) a.trace[(size_t)blockIdx.x * kTracePoints + k] = t;
+    }
+}
+
 // Page id entry `v` of a page-table row, clamped into [0, num_pages).
 __device__ __forceinline__ int checked_page(const KernelArgs& a, int v) {
     if ((unsigned)v >= (unsigned)a.num_pages) {
@@ -374,13 +386,41 @@ __host__ __device__ constexpr size_t epilogue_floats(int D, int slots_per_group,
                                    (size_t)(token_groups - 1) * slots_per_group * 16 * (D + 8);
 }
 
+// Device-scope accesses for the split partials when the last split of a (request, kv head)
+// combines them inside the attention kernel. The stores write through to where every compute
+// unit's loads see them once they complete, and the loads read there, so the hand-off needs no
+// cache-wide release or acquire (an L2 write-back or invalidate): only each storing wave's wait
+// for its stores to complete before the arrival counter moves.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev4(float* p, f32x4_t v) {
+    uint64_t* q = reinterpret_cast<uint64_t*>(p);
+    __hip_atomic_store(q, (uint64_t)__float_as_uint(v[0]) | ((uint64_t)__float_as_uint(v[1]) << 32), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, (uint64_t)__float_as_uint(v[2]) | ((uint64_t)__float_as_uint(v[3]) << 32),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Sixteen bytes at byte offset `off` of a buffer, read at device scope (the sc1 cache policy).
+constexpr int kCachePolicyDevice = 16;
+__device__ __forceinline__ f32x4_t ld_dev4(__amdgpu_buffer_rsrc_t buf, uint32_t off) {
+    return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(buf, off, 0, kCachePolicyDevice));
+}
+// Raw buffer resource over `bytes` bytes at p (gfx9 descriptor word 3 for untyped dword access).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
 // Store one wave's rows: acc holds O^T fragments (lane: query row r16 of block n,
 // dims db*16 + 4*quad .. +3), already scaled to the row's final weights when
 // `final`, else relative to 2^m. m, l: the row's reference maximum (log2 units)
-// and weight sum.
+// and weight sum. dev: partials go out with device-scope stores (combined in-kernel).
 template <int D>
 __device__ __forceinline__ void store_rows(const KernelArgs& a, const Unit& u, int r, bool final, const f32x4_t (&acc)[D / 16],
-                                           float m, float l, int quad) {
+                                           float m, float l, int quad, bool dev) {
     constexpr int DB = D / 16;
     if (r >= a.R || u.rg * a.R + r >= a.R_all) return;
     f32x4_t acc_s[DB];
@@ -388,11 +428,20 @@ __device__ __forceinline__ void store_rows(const KernelArgs& a, const Unit& u, i
     for (int db = 0; db < DB; ++db) acc_s[db] = acc[db] * a.v_scale;  // a stored value stands for v_scale * v
     if (!final) {
         const size_t pr = (size_t)blockIdx.x * a.R + r;
+        if (dev) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) *(f32x4_t*)(a.part_acc + pr * D + db * 16 + quad * 4) = acc_s[db];
-        if (quad == 0) {
-            a.part_m[pr] = m;
-            a.part_l[pr] = l;
+            for (int db = 0; db < DB; ++db) st_dev4(a.part_acc + pr * D + db * 16 + quad * 4, acc_s[db]);
+            if (quad == 0) {
+                st_dev(a.part_m + pr, m);
+                st_dev(a.part_l + pr, l);
+            }
+        } else {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) *(f32x4_t*)(a.part_acc + pr * D + db * 16 + quad * 4) = acc_s[db];
+            if (quad == 0) {
+                a.part_m[pr] = m;
+                a.part_l[pr] = l;
+            }
         }
         return;
     }
@@ -408,9 +457,103 @@ __device__ __forceinline__ void store_rows(const KernelArgs& a, const Unit& u, i
     if (quad == 0 && a.lse) a.lse[orow] = l == 0.f ? kNegInf : m + log2f(l);  // a NaN sum stays NaN
 }
 
+// Floats of LDS the in-kernel combine needs for S splits of R rows: the arrival flag, per-row
+// maximum and weight sum, and each split's exponent and weight sum per row.
+__host__ __device__ constexpr size_t last_arriver_floats(int S, int R) { return 4 + (size_t)2 * R + (size_t)2 * S * R; }
+
+// The split combine inside the attention kernel, by the last unit of a (request, kv head,
+// row group) to finish (the multi-CTA split-KV of TensorRT-LLM PR #20374, Description: the
+// splits of a decode row meet through counter buffers). Every unit of a split pair has
+// stored its partial with device-scope stores; each storing wave waits for them to complete,
+// then one thread adds 1 to the pair's arrival counter. The unit that brings the counter to
+// S resets it for the next call and combines the S partials in split order: per row
+// M = max m_s, L = sum 2^(m_s - M) l_s, out = sum 2^(m_s - M) acc_s / L, lse = M + log2 L. An
+// empty split (m = -inf) weighs 0; 0 * NaN still carries a NaN sum through. No unit waits for
+// another: the last arriver only reads what has already completed.
+template <int D>
+__device__ void combine_if_last(const KernelArgs& a, const Unit& u, float* lds) {
+    constexpr int DL = D / 4;  // float4 columns of a row
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int S = u.S, R = a.R;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have completed
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();  // every wave's have; the epilogue is done with LDS
+    int* flag = reinterpret_cast<int*>(lds);
+    if (tid == 0) {
+        const int pair = (u.b * a.Hkv + u.hk) * a.row_groups + u.rg;
+        const uint32_t old = __hip_atomic_fetch_add(a.counters + pair, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = old == (uint32_t)(S - 1);
+        if (last) __hip_atomic_store(a.counters + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = last;
+    }
+    __syncthreads();
+    if (*flag == 0) return;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+
+    const int u0 = blockIdx.x - u.s;  // the pair's units are consecutive
+    float* rowM = lds + 4;
+    float* rowL = rowM + R;
+    float* em = rowL + R;   // [S][R] exponents m_s, then weights 2^(m_s - M) / L
+    float* el = em + S * R;  // [S][R] weight sums l_s
+    // Row statistics: TPR threads per row, each folding every TPR-th split; the TPR threads of a
+    // row are consecutive lanes of one wave and meet by butterfly shuffles.
+    int tpr = 1;
+    while (tpr * 2 <= 64 && tpr * 2 * R <= nt) tpr *= 2;
+    const int r = tid / tpr, j = tid - (tid / tpr) * tpr;
+    const bool row_on = r < R;
+    float M = kNegInf;
+    if (row_on)
+        for (int s = j; s < S; s += tpr) {
+            const size_t pr = (size_t)(u0 + s) * R + r;
+            const float ms = ld_dev(a.part_m + pr), ls = ld_dev(a.part_l + pr);
+            em[s * R + r] = ms;
+            el[s * R + r] = ls;
+            M = fmaxf(M, ms);
+        }
+    for (int off = tpr >> 1; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    float L = 0.f;
+    if (row_on)
+        for (int s = j; s < S; s += tpr) {
+            const float ms = em[s * R + r];
+            L += (ms == kNegInf ? 0.f : fast_exp2(ms - M)) * el[s * R + r];
+        }
+    for (int off = tpr >> 1; off > 0; off >>= 1) L += __shfl_xor(L, off, 64);
+    if (row_on) {
+        const float inv = L == 0.f ? 0.f : 1.f / L;  // no keys: zeros; a NaN sum stays NaN
+        for (int s = j; s < S; s += tpr) {
+            const float ms = em[s * R + r];
+            em[s * R + r] = (ms == kNegInf ? 0.f : fast_exp2(ms - M)) * inv;
+        }
+        if (j == 0) {
+            rowM[r] = M;
+            rowL[r] = L;
+        }
+    }
+    __syncthreads();
+    // Outputs: one float4 column of one row per item, summed over the splits in order. The pair's
+    // partials are S consecutive [R][D] blocks: one buffer resource covers them (byte offsets).
+    const __amdgpu_buffer_rsrc_t accs = make_rsrc(a.part_acc + (size_t)u0 * R * D, (uint32_t)((size_t)S * R * D * 4));
+    for (int it = tid; it < R * DL; it += nt) {
+        const int rr = it / DL, c = (it - (it / DL) * DL) * 4;
+        const int rk = u.rg * R + rr;
+        if (rk >= a.R_all) continue;
+        f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+        const uint32_t base = (uint32_t)((rr * D + c) * 4), step = (uint32_t)(R * D * 4);
+#pragma unroll 16
+        for (int s = 0; s < S; ++s) o += ld_dev4(accs, base + (uint32_t)s * step) * em[s * R + rr];
+        const int i = rk / a.g, h = u.hk * a.g + (rk - (rk / a.g) * a.g);
+        const size_t orow = (size_t)(u.b * a.K + i) * a.Hq + h;
+        const uint32_t lo = f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
+        const uint32_t hi = f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
+        *(u32x2_t*)(a.out + orow * D + c) = u32x2_t{lo, hi};
+        if (c == 0 && a.lse) a.lse[orow] = rowL[rr] == 0.f ? kNegInf : rowM[rr] + log2f(rowL[rr]);
+    }
+}
+
 // Epilogue of a unit: merge the token groups' softmax states, then write the
 // unit's partial (a split request) or the final bf16 output and base-2 LSE.
 // With one token group every wave owns whole rows and stores from registers.
+// Every wave of the workgroup runs to the end (the in-kernel combine has barriers).
 template <int D, int NBW, bool WINDOWED, bool ALL_ON>
 __device__ void finish_unit(const KernelArgs& a, const Unit& u, WaveRows<D, NBW, WINDOWED, ALL_ON>& w, int tg,
                             int wr, int WT, int WR, float* lds) {
@@ -419,6 +562,7 @@ __device__ void finish_unit(const KernelArgs& a, const Unit& u, WaveRows<D, NBW,
     const int lane = tid & 63, r16 = lane & 15, quad = lane >> 4;
     const int slots = WR * NBW;  // row blocks per token group
     const bool final = u.S <= 1;
+    const bool fused = !final && a.fused_combine;
 
 #pragma unroll
     for (int n = 0; n < NBW; ++n) w.l[n] = quad_sum(w.l[n]);
@@ -431,59 +575,65 @@ __device__ void finish_unit(const KernelArgs& a, const Unit& u, WaveRows<D, NBW,
             const float inv = final ? (l == 0.f ? 0.f : 1.f / l) : 1.f;  // no keys: zeros; a NaN sum stays NaN
 #pragma unroll
             for (int db = 0; db < DB; ++db) w.acc[n][db] *= inv;
-            store_rows<D>(a, u, (wr * NBW + n) * 16 + r16, final, w.acc[n], w.m[n], l, quad);
+            store_rows<D>(a, u, (wr * NBW + n) * 16 + r16, final, w.acc[n], w.m[n], l, quad, fused);
         }
-        return;
+    } else {
+        float* ml = lds;                                   // [WT][slots * 16][2]
+        float* xa = lds + (size_t)WT * slots * 16 * 2;     // [WT - 1][slots * 16][XP]
+        __syncthreads();  // tile buffers are free from here on
+        trace_point(a, kTrEpilogue);
+#pragma unroll
+        for (int n = 0; n < NBW; ++n)
+            if (quad == 0) {
+                float* e = ml + ((size_t)(tg * slots + wr * NBW + n) * 16 + r16) * 2;
+                e[0] = w.m[n];
+                e[1] = w.l[n];
+            }
+        __syncthreads();
+        float rowM[NBW], rowL[NBW];
+#pragma unroll
+        for (int n = 0; n < NBW; ++n) {
+            const int srow = (wr * NBW + n) * 16 + r16;
+            float M = kNegInf;
+            for (int t = 0; t < WT; ++t) M = fmaxf(M, ml[((size_t)t * slots * 16 + srow) * 2]);
+            // A group with no keys (m = -inf) weighs 0; 0 * NaN still carries a NaN sum through.
+            float L = 0.f;
+            for (int t = 0; t < WT; ++t) {
+                const float* e = ml + ((size_t)t * slots * 16 + srow) * 2;
+                L += (e[0] == kNegInf ? 0.f : fast_exp2(e[0] - M)) * e[1];
+            }
+            float alpha = w.m[n] == kNegInf ? 0.f : fast_exp2(w.m[n] - M);
+            if (final) alpha = L == 0.f ? 0.f : alpha / L;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) w.acc[n][db] *= alpha;
+            rowM[n] = M;
+            rowL[n] = L;
+            if (tg > 0) {
+                float* x = xa + ((size_t)(tg - 1) * slots * 16 + srow) * XP;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) *(f32x4_t*)(x + db * 16 + quad * 4) = w.acc[n][db];
+            }
+        }
+        __syncthreads();
+        if (tg == 0) {
+#pragma unroll
+            for (int n = 0; n < NBW; ++n) {
+                if (!ALL_ON && !w.on[n]) continue;
+                const int srow = (wr * NBW + n) * 16 + r16;
+                for (int t = 1; t < WT; ++t) {
+                    const float* x = xa + ((size_t)(t - 1) * slots * 16 + srow) * XP;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) w.acc[n][db] += *(const f32x4_t*)(x + db * 16 + quad * 4);
+                }
+                store_rows<D>(a, u, srow, final, w.acc[n], rowM[n], rowL[n], quad, fused);
+            }
+        }
     }
-
-    float* ml = lds;                                   // [WT][slots * 16][2]
-    float* xa = lds + (size_t)WT * slots * 16 * 2;     // [WT - 1][slots * 16][XP]
-    __syncthreads();  // tile buffers are free from here on
-#pragma unroll
-    for (int n = 0; n < NBW; ++n)
-        if (quad == 0) {
-            float* e = ml + ((size_t)(tg * slots + wr * NBW + n) * 16 + r16) * 2;
-            e[0] = w.m[n];
-            e[1] = w.l[n];
-        }
-    __syncthreads();
-    float rowM[NBW], rowL[NBW];
-#pragma unroll
-    for (int n = 0; n < NBW; ++n) {
-        const int srow = (wr * NBW + n) * 16 + r16;
-        float M = kNegInf;
-        for (int t = 0; t < WT; ++t) M = fmaxf(M, ml[((size_t)t * slots * 16 + srow) * 2]);
-        // A group with no keys (m = -inf) weighs 0; 0 * NaN still carries a NaN sum through.
-        float L = 0.f;
-        for (int t = 0; t < WT; ++t) {
-            const float* e = ml + ((size_t)t * slots * 16 + srow) * 2;
-            L += (e[0] == kNegInf ? 0.f : fast_exp2(e[0] - M)) * e[1];
-        }
-        float alpha = w.m[n] == kNegInf ? 0.f : fast_exp2(w.m[n] - M);
-        if (final) alpha = L == 0.f ? 0.f : alpha / L;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) w.acc[n][db] *= alpha;
-        rowM[n] = M;
-        rowL[n] = L;
-        if (tg > 0) {
-            float* x = xa + ((size_t)(tg - 1) * slots * 16 + srow) * XP;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) *(f32x4_t*)(x + db * 16 + quad * 4) = w.acc[n][db];
-        }
+    if (a.trace) {
+        __syncthreads();
+        trace_point(a, kTrStored);
     }
-    __syncthreads();
-    if (tg != 0) return;
-#pragma unroll
-    for (int n = 0; n < NBW; ++n) {
-        if (!ALL_ON && !w.on[n]) continue;
-        const int srow = (wr * NBW + n) * 16 + r16;
-        for (int t = 1; t < WT; ++t) {
-            const float* x = xa + ((size_t)(t - 1) * slots * 16 + srow) * XP;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) w.acc[n][db] += *(const f32x4_t*)(x + db * 16 + quad * 4);
-        }
-        store_rows<D>(a, u, srow, final, w.acc[n], rowM[n], rowL[n], quad);
-    }
+    if (fused) combine_if_last<D>(a, u, lds);
 }
 
 // Store the block's keys and values (dense bf16 [B, K, Hkv, D]) of this unit's
@@ -539,7 +689,9 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
     const int r16 = lane & 15, quad = lane >> 4;
     const int WT = a.token_groups, WR = a.row_waves;
     const int tg = wave / WR, wr = wave - (wave / WR) * WR;  // token group, row group
+    trace_point(a, kTrEntry);
     const Unit u = decode_unit<WINDOWED>(a);
+    trace_point(a, kTrLength);
     WaveRows<D, NBW, WINDOWED, ALL_ON> w;
     w.template init<FP8>(a, u, wr * NBW, lane);
     // LDS: [one V tile per wave] [page-id window]
@@ -577,6 +729,7 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
             }
         }
         __syncthreads();
+        if (win == u.ulo) trace_point(a, kTrPages);
         const int nk = span > tg ? (span - tg + WT - 1) / WT : 0;
         if (nk == 0) continue;
 
@@ -724,6 +877,7 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
         }
         if (a.append && u.rg == 0) append_block<D, FP8>(a, u);
     }
+    if (wave == 0) trace_point(a, kTrLoop);
     finish_unit(a, u, w, tg, wr, WT, WR, reinterpret_cast<float*>(lds));
 }
 
@@ -757,7 +911,9 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, quad = lane >> 4;
+    trace_point(a, kTrEntry);
     const Unit u = decode_unit<WINDOWED>(a);
+    trace_point(a, kTrLength);
     WaveRows<D, NBW, WINDOWED, ALL_ON> w;
     w.init(a, u, wave * NBW, lane);
     int* pid_tab = reinterpret_cast<int*>(lds + 2 * SLOT);
@@ -825,6 +981,7 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
             }
         }
         __syncthreads();
+        if (win == u.ulo) trace_point(a, kTrPages);
         const int nk = span;
 
         // A tile is NBLK blocks of 64 16-byte pieces in four parts (K rows 0-15,
@@ -925,6 +1082,7 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
         compute_at(u.C, 0, std::true_type{});
         if (a.append && u.rg == 0) append_block<D, FP8>(a, u);
     }
+    if (wave == 0) trace_point(a, kTrLoop);
     finish_unit(a, u, w, 0, wave, 1, WR, reinterpret_cast<float*>(lds));
 }
 

@@ -35,6 +35,8 @@ struct KernelArgs {
     float* part_l;
     float* part_acc;
     uint32_t* err;         // input-error word: bits kErrLength / kErrPage are set when a clamp was needed
+    uint32_t* counters;    // per (request, kv head, row group): arrivals of its units; zero between calls
+    int32_t fused_combine; // split pairs are combined in the attention kernel by their last unit
     uint16_t* out;
     float* lse;
     int32_t K, Hq, Hkv, g, R, P, stride, num_pages;  // R: query rows per work unit (<= 128)
@@ -55,7 +57,14 @@ struct KernelArgs {
     float block_scale_log2;  // sm_scale * log2(e): logit scale of the dense block keys (they are unscaled)
     float block_p_mul;       // 1 / v_scale: the dense block values join the accumulator, which is kept in
                              // stored units, through probabilities multiplied by this
+    uint64_t* trace;         // NULL, or kTracePoints timestamps per work unit (profiling aid)
 };
+
+// Phase timestamps a traced attention kernel records per work unit (workgroup), in the
+// 100 MHz constant clock: kernel entry, length known, page ids staged, this unit's loop done
+// (token group 0), all token groups done (epilogue start), stores complete.
+constexpr int kTracePoints = 8;
+enum TracePoint { kTrEntry = 0, kTrLength = 1, kTrPages = 2, kTrLoop = 3, kTrEpilogue = 4, kTrStored = 5 };
 
 // Chosen kernel shape for a plan.
 struct KernelShape {
@@ -71,6 +80,8 @@ struct KernelShape {
 };
 
 size_t attention_lds_bytes(const KernelShape& s, int R);
+// Floats of LDS the in-kernel split combine needs for S splits of R rows.
+size_t last_arriver_lds_floats(int S, int R);
 
 hipError_t launch_attention(const KernelShape& shape, bool windowed, int units, const KernelArgs& args,
                             hipStream_t stream);

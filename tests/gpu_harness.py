@@ -47,7 +47,8 @@ def upload(inputs: synth.Inputs, device="cuda") -> DeviceCase:
                       torch.from_numpy(np.ascontiguousarray(inputs.seq_lens)).to(device))
 
 
-def params_for(dc: DeviceCase, *, window_left=None, window_right=None, splits=0, scale=None, waves=0):
+def params_for(dc: DeviceCase, *, window_left=None, window_right=None, splits=0, scale=None, waves=0,
+               combine="auto"):
     c = dc.inputs.case
     return ba.make_params(batch=c.batch, block_size=c.block_size, num_q_heads=c.num_q_heads,
                           num_kv_heads=c.num_kv_heads, head_dim=c.head_dim, page_size=c.page_size,
@@ -56,14 +57,15 @@ def params_for(dc: DeviceCase, *, window_left=None, window_right=None, splits=0,
                           window_left=c.window_left if window_left is None else window_left,
                           window_right=c.window_right if window_right is None else window_right,
                           splits_override=splits, waves_override=waves, kv_dtype=c.kv_dtype, k_scale=c.k_scale,
-                          v_scale=c.v_scale)
+                          v_scale=c.v_scale, combine=combine)
 
 
 def run(dc: DeviceCase, *, window_left=None, window_right=None, splits=0, plan_lens=None, with_lse=True,
-        canary=False, waves=0):
+        canary=False, waves=0, combine="auto"):
     """Plan + forward on the current stream; returns (out float32 np, lse np or None, info)."""
     c = dc.inputs.case
-    prm = params_for(dc, window_left=window_left, window_right=window_right, splits=splits, waves=waves)
+    prm = params_for(dc, window_left=window_left, window_right=window_right, splits=splits, waves=waves,
+                     combine=combine)
     lens = dc.inputs.seq_lens if plan_lens is None else plan_lens
     nbytes = ba.blockattn_workspace_size(prm, lens)
     guard = 4096 if canary else 0

@@ -25,8 +25,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layouts_match_header():
-    # params: 13 int32 + 3 float = 64 bytes; info: 11 int32 + padding + size_t = 56 bytes
-    assert ctypes.sizeof(ba.blockattn_params) == 64
+    # params: 14 int32 + 3 float = 68 bytes; info: 12 int32 + size_t = 56 bytes
+    assert ctypes.sizeof(ba.blockattn_params) == 68
     assert ctypes.sizeof(ba.blockattn_plan_info_t) == 56
 
 
@@ -238,3 +238,23 @@ def test_merge_checks_its_arguments():
     assert call(2, 10, 64, one, one, None) == ba.BLOCKATTN_ERR_INVALID_ARGUMENT
     assert call(2, 10, 64, one, one, vp(0x1000 + 64)) == ba.BLOCKATTN_ERR_INVALID_ARGUMENT  # overlaps part_out
     assert "overlap" in ba.blockattn_last_error()
+
+
+def test_combine_mode_plan_choice():
+    lens = [131079, 131079]
+    auto = plan_info(params(page_table_stride=4200), lens)
+    assert auto["max_splits"] > 1 and auto["fused_combine"] == 0 and auto["combine_launch"] == 1
+    last = plan_info(params(page_table_stride=4200, combine="last_arriver"), lens)
+    assert last["fused_combine"] == 1 and last["combine_launch"] == 0
+    kern = plan_info(params(page_table_stride=4200, combine="kernel"), lens)
+    assert kern["fused_combine"] == 0 and kern["combine_launch"] == 1
+    # one split per request: nothing to combine, whatever the mode
+    one = plan_info(params(page_table_stride=4200, combine="last_arriver", splits_override=1), lens)
+    assert one["fused_combine"] == 0 and one["combine_launch"] == 0
+    # the in-kernel combine keeps every split's statistics in LDS: too many splits are refused
+    with pytest.raises(ba.BlockAttnError) as e:
+        ba.blockattn_plan(params(page_table_stride=4200, combine="last_arriver", splits_override=4000), lens)
+    assert e.value.status == ba.BLOCKATTN_ERR_UNSUPPORTED and "LDS" in e.value.message
+    with pytest.raises(ba.BlockAttnError) as e:
+        ba.blockattn_plan(params(combine=3), [100, 100])
+    assert e.value.status == ba.BLOCKATTN_ERR_INVALID_ARGUMENT and "combine_mode" in e.value.message
