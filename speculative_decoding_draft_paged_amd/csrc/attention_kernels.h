@@ -406,6 +406,7 @@ __device__ __forceinline__ float ld_dev(const float* p) {
 }
 // Sixteen bytes at byte offset `off` of a buffer, read at device scope (the sc1 cache policy).
 constexpr int kCachePolicyDevice = 16;
+constexpr int kCachePolicyStream = 2;  // non-temporal: each byte of the pools is read once per call
 __device__ __forceinline__ f32x4_t ld_dev4(__amdgpu_buffer_rsrc_t buf, uint32_t off) {
     return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(buf, off, 0, kCachePolicyDevice));
 }
@@ -885,12 +886,18 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
 // Shared-tile main loop for many query rows (R > 32): WR row-waves, each owning up
 // to NBW row blocks, all consume every tile of the unit. Where each row-wave loading
 // its own copy of a tile would leave only about one tile of unique bytes in flight
-// per workgroup, here the workgroup loads each tile once: each wave moves LPT
+// per workgroup, here the workgroup loads each tile once: each wave moves up to LPT
 // 1-KiB blocks of K and V (16 bytes per lane), DR tiles ahead of the one being
-// consumed, into a two-slot LDS ring (row-major, padded pitch). One workgroup
+// consumed, into a three-slot LDS ring (row-major, padded pitch). One workgroup
 // barrier per tile orders the ring; it waits on LDS traffic only, so the DR tiles
-// of global loads stay in flight across it. Loads sit at fixed places (the tile
-// index is clamped past the unit's end), so each wait names exactly one tile.
+// of global loads stay in flight across it.
+// Pipelined across tiles: while a wave runs the softmax and PV product of tile t, the
+// score MFMAs of tile t + 1 are already issued (its keys sit in the next ring slot), so
+// the matrix cores and the vector ALUs of a SIMD work on different tiles at once.
+// Every load sits at a fixed place, so each wait names exactly one tile. Loads that
+// would fall past the unit's last tile, or past the tile's last block, go through a
+// buffer resource with no records: the instruction runs (the wait counts stay exact)
+// but reads nothing from memory and returns zeros.
 template <int D, int NBW, bool WINDOWED, bool ALL_ON, int WR, int DR, bool FP8>
 __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared_kernel(const KernelArgs a) {
     constexpr int NT = 64 * WR;
@@ -904,7 +911,9 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
     constexpr int KP = kKPitch<D>;        // padded row pitch (bf16) of the K tile in LDS
     constexpr int VP = kVPitch<D>;        // and of the V tile
     constexpr int SLOT = T * (KP + VP);   // bf16 elements per ring slot: K tile, then V tile
+    constexpr int NSLOT = 3;              // ring slots
     constexpr int DB = D / 16, KK = D / 32;
+    static_assert(DR >= 2, "the prologue stages two tiles");
 
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
     const int tid = threadIdx.x;
@@ -916,7 +925,7 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
     trace_point(a, kTrLength);
     WaveRows<D, NBW, WINDOWED, ALL_ON> w;
     w.init(a, u, wave * NBW, lane);
-    int* pid_tab = reinterpret_cast<int*>(lds + 2 * SLOT);
+    int* pid_tab = reinterpret_cast<int*>(lds + NSLOT * SLOT);
 
     const int32_t* pt_row = a.page_table + (size_t)u.b * a.stride;
     const int last_page = max(u.NC - 1, 0) >> a.p_shift;
@@ -931,32 +940,25 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
         u32x4_t c[LPT];
     };
 
-    // Scores, softmax update and PV for the tile at token t0 held in ring slot `slot`.
-    // dense: the tile holds the block's unscaled keys and values from the dense arrays
-    auto compute_at = [&](int t0, int slot, auto dense) {
+    // Key fragments (A operand of S^T = K Q^T) of the tile in ring slot `slot`.
+    auto read_k = [&](int slot, bf16x8_t (&kf)[2][KK]) {
         const uint16_t* kl = lds + slot * SLOT;
-        const uint16_t* vl = kl + T * KP;
-        bf16x8_t kf[2][KK];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
                 kf[mb][kk] =
                     __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(kl + (mb * 16 + r16) * KP + kk * 32 + quad * 8));
-        f32x4_t s[NBW][2];
-        w.scores(kf, s);
-        bf16x8_t vf[DB];
-        const uint16_t* vrow = vl + (4 * quad + (r16 >> 2)) * VP + 4 * (r16 & 3);
+    };
+    // Value fragments (V^T, transposed from the row-major tile) of the tile in ring slot `slot`.
+    auto read_v = [&](int slot, bf16x8_t (&vf)[DB]) {
+        const uint16_t* vrow = lds + slot * SLOT + T * KP + (4 * quad + (r16 >> 2)) * VP + 4 * (r16 & 3);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             const u32x2_t lo = lds_read_tr16(vrow + db * 16);
             const u32x2_t hi = lds_read_tr16(vrow + 16 * VP + db * 16);
             vf[db] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
         }
-        if constexpr (decltype(dense)::value)
-            w.template update<true>(s, vf, t0, a.block_scale_log2, quad, a.block_p_mul);
-        else
-            w.update(s, vf, t0, a.scale_log2, quad);
     };
 
     for (int win = u.ulo; win < u.uhi; win += kPidWindow) {
@@ -986,11 +988,13 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
 
         // A tile is NBLK blocks of 64 16-byte pieces in four parts (K rows 0-15,
         // K rows 16-31, V rows 0-15, V rows 16-31) of BP blocks each. Wave w moves
-        // blocks w, w + WR, ... (clamped: a wave past the last block repeats it, writing
-        // the same bytes to the same place), so each block's part, page and bases are
-        // wave-uniform scalars and a lane's offset inside a block is fixed.
+        // blocks w, w + WR, ..., so each block's part, page and bases are wave-uniform
+        // scalars and a lane's offset inside a block is fixed. A wave's slot past the last
+        // block, and every block of a tile past the unit's end, reads through an empty
+        // buffer resource (zeros, no memory traffic) and is not stored.
         auto issue = [&](Stage& st, int t) {
-            const int tc = min(t, nk - 1);
+            const bool real = t < nk;
+            const int tc = real ? t : nk - 1;
             const int sl0 = __builtin_amdgcn_readfirstlane(pid_tab[2 * tc]);
             const int sl1 = __builtin_amdgcn_readfirstlane(pid_tab[2 * tc + 1]);
             const int t0 = (win + tc) * T;
@@ -998,11 +1002,13 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
             const size_t slab1 = ((size_t)sl1 << (a.p_shift + kLog2<D>)) + (size_t)(((t0 + 16) & pmask) * D);
 #pragma unroll
             for (int k = 0; k < LPT; ++k) {
-                const int b = min(wave + k * WR, NBLK - 1);
+                const int bw = wave + k * WR;
+                const int b = min(bw, NBLK - 1);
                 const int part = b / BP;
                 const char* base = static_cast<const char*>((part >> 1) ? a.vc : a.kc) +
                                    (((part & 1) ? slab1 : slab0) + (size_t)(b % BP) * RPB * D) * EB;
-                st.c[k] = __builtin_nontemporal_load((const u32x4_t*)(base + lane_goff));
+                const int bytes = (real && bw < NBLK) ? 64 * 16 : 0;
+                st.c[k] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(base, bytes), lane_goff, 0, kCachePolicyStream);
             }
         };
         auto store = [&](const Stage& st, int t, int slot) {
@@ -1011,7 +1017,9 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
             char* dst = reinterpret_cast<char*>(lds + slot * SLOT);
 #pragma unroll
             for (int k = 0; k < LPT; ++k) {
-                const int b = min(wave + k * WR, NBLK - 1);
+                const int bw = wave + k * WR;
+                if (k * WR >= NBLK - (WR - 1) && bw >= NBLK) continue;  // this wave has no block here
+                const int b = bw;
                 const int part = b / BP;
                 const int row0 = (part & 1) * 16 + (b % BP) * RPB;  // first tile row of the block
                 // the lane's LE elements as bf16: one 16-byte piece, or two for fp8
@@ -1035,11 +1043,11 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
                 }
             }
         };
-        auto compute = [&](int t, int slot) { compute_at((win + t) * T, slot, std::false_type{}); };
 
-        // Tile t waits in st[t % DR] until it is written to ring slot t & 1. The
-        // scheduling barriers keep the loads of successive tiles in tile order, so the
-        // counter wait before each store covers exactly the oldest tile.
+        // Tile t waits in st[t % DR] until it is written to ring slot t % 3, two
+        // iterations before it is consumed. The scheduling barriers keep the loads of
+        // successive tiles in tile order, so the counter wait before each store covers
+        // exactly the oldest tile.
         Stage st[DR];
 #pragma unroll
         for (int j = 0; j < DR; ++j) {
@@ -1049,16 +1057,44 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
         store(st[0], 0, 0);
         issue(st[0], DR);
         __builtin_amdgcn_sched_barrier(0);
+        store(st[1], 1, 1);
+        issue(st[1], DR + 1);
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
+        f32x4_t s_cur[NBW][2];
+        {
+            bf16x8_t kf[2][KK];
+            read_k(0, kf);
+            w.scores(kf, s_cur);
+        }
+        int slot = 0;  // ring slot of tile t
         for (int tb = 0; tb < nk; tb += DR) {
 #pragma unroll
             for (int j = 0; j < DR; ++j) {
                 const int t = tb + j;
-                if (t < nk) compute(t, t & 1);
-                store(st[(j + 1) % DR], t + 1, (t + 1) & 1);
-                issue(st[(j + 1) % DR], t + 1 + DR);
+                const int slot1 = slot == NSLOT - 1 ? 0 : slot + 1;    // tile t + 1
+                const int slot2 = slot1 == NSLOT - 1 ? 0 : slot1 + 1;  // tile t + 2 (held tile t - 1)
+                if (t < nk) {
+                    // scores of tile t + 1 first (past the end: zeros, unused), then the
+                    // softmax and PV product of tile t
+                    f32x4_t s_next[NBW][2];
+                    bf16x8_t kf[2][KK];
+                    read_k(slot1, kf);
+                    w.scores(kf, s_next);
+                    bf16x8_t vf[DB];
+                    read_v(slot, vf);
+                    w.update(s_cur, vf, (win + t) * T, a.scale_log2, quad);
+#pragma unroll
+                    for (int n = 0; n < NBW; ++n) {
+                        s_cur[n][0] = s_next[n][0];
+                        s_cur[n][1] = s_next[n][1];
+                    }
+                }
+                store(st[(j + 2) % DR], t + 2, slot2);
+                issue(st[(j + 2) % DR], t + 2 + DR);
                 __builtin_amdgcn_sched_barrier(0);
                 __syncthreads();
+                slot = slot1;
             }
         }
     }
@@ -1079,7 +1115,15 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
         }
         __syncthreads();
         w.hi_cap = u.N;
-        compute_at(u.C, 0, std::true_type{});
+        {
+            bf16x8_t kf[2][KK];
+            read_k(0, kf);
+            f32x4_t sb[NBW][2];
+            w.scores(kf, sb);
+            bf16x8_t vf[DB];
+            read_v(0, vf);
+            w.template update<true>(sb, vf, u.C, a.block_scale_log2, quad, a.block_p_mul);
+        }
         if (a.append && u.rg == 0) append_block<D, FP8>(a, u);
     }
     if (wave == 0) trace_point(a, kTrLoop);

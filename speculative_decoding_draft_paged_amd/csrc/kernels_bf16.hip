@@ -40,7 +40,7 @@ size_t attention_lds_bytes(const KernelShape& s, int R) {
     const int D = s.head_dim;
     if (s.shared) {
         const size_t pitches = D == 64 ? kKPitch<64> + kVPitch<64> : kKPitch<128> + kVPitch<128>;
-        const size_t ring = (size_t)2 * kTileTokens * pitches * sizeof(uint16_t) + 2 * kPidWindow * sizeof(int);
+        const size_t ring = (size_t)3 * kTileTokens * pitches * sizeof(uint16_t) + 2 * kPidWindow * sizeof(int);
         const size_t epi = epilogue_floats(D, s.row_waves * s.nbw, 1) * sizeof(float);
         return ring > epi ? ring : epi;
     }
