@@ -152,7 +152,7 @@ int tiles_for(const blockattn_params* p, int n) {
     return (n + kTileTokens - 1) / kTileTokens - lo / kTileTokens;
 }
 
-KernelShape choose_shape(int D, int NB, int R, int waves_override) {
+KernelShape choose_shape(int D, int NB, int R, int waves_override, long total_tiles) {
     // Each wave owns up to two 16-row blocks of the R query rows. With one row-wave
     // (R <= 32), WT token groups of the workgroup stream different tiles, each wave
     // loading its own (stream_kernel). With WR > 1 row-waves the workgroup loads each
@@ -172,13 +172,30 @@ KernelShape choose_shape(int D, int NB, int R, int waves_override) {
     // 0.5-4 % over the unwindowed batches measured (one 8-wave workgroup per CU instead
     // of two of 4 waves) and tie on the wider ones.
     s.token_groups = s.shared ? 1 : std::max(1, max_waves / s.row_waves);
-    if (s.shared && D == 128) {
+    const bool many_tiles = total_tiles >= 8L * kNumCUs;
+    if (s.shared && D == 128 && NB >= 7 && (waves_override > NB || (waves_override == 0 && many_tiles))) {
+        // Seven or eight row blocks and at least 8 tiles per CU: two token groups, each
+        // of four waves with two row blocks per wave and its own ring (8 waves, two per
+        // SIMD within 256 registers each). Two blocks per wave halve the LDS reads per
+        // row, and the second group keeps two waves on every SIMD. Measured at seven
+        // blocks (windowed, W = 4096, D = 128), per call against seven one-block waves:
+        // 64 requests x 4 kv heads of 2K-16K keys 131 against 145 us; one kv head, 64
+        // requests of 2K, 8K, 16K keys 35.8 / 50.0 / 48.4 against 39.4 / 53.9 / 52.2 us;
+        // 8 requests of 16K keys (about 4 tiles per CU) 27.3 against 24.4 us, so
+        // smaller batches keep the one-group shape.
+        s.nbw = 2;
+        s.row_waves = (NB + 1) / 2;
+        s.all_on = NB % 2 == 0;
+        s.token_groups = 2;
+        s.waves_per_simd = 2;
+    } else if (s.shared && D == 128) {
         // One row block per wave, up to 8 waves (two per SIMD, each within 256
         // registers), so two waves per SIMD hide each other's latency. Measured on the
         // windowed mixed batch: at three row blocks, three waves of one block beat two
         // waves of two (121 against 138 us per call); at seven, seven waves beat four
         // (151 against 197 us). waves_override picks the waves per workgroup: rows per
-        // wave = ceil(blocks / waves), 1 or 2.
+        // wave = ceil(blocks / waves), 1 or 2; above the row blocks (seven or more), the
+        // two token groups.
         int wv = NB;
         if (waves_override > 0) wv = std::max((NB + 1) / 2, std::min(waves_override, NB));
         s.nbw = (NB + wv - 1) / wv;
@@ -209,8 +226,6 @@ int build_plan(const blockattn_params* p, const int32_t* lens, blockattn_plan_s*
     pl->G = (blocks_all + kMaxRowBlocks - 1) / kMaxRowBlocks;
     pl->NB = (blocks_all + pl->G - 1) / pl->G;
     pl->R = pl->G == 1 ? pl->R_all : 16 * pl->NB;
-    pl->shape = choose_shape(p->head_dim, pl->NB, pl->R, p->waves_override);
-    pl->shape.fp8 = p->kv_dtype == BLOCKATTN_KV_FP8_E4M3;
     pl->merge_active = pl->kind == 1 && p->block_size > 1 && p->window_right != 0;
 
     const int B = p->batch, H = p->num_kv_heads * pl->G;  // (kv head, row group) pairs per request
@@ -220,6 +235,8 @@ int build_plan(const blockattn_params* p, const int32_t* lens, blockattn_plan_s*
         nt[b] = tiles_for(p, lens[b]);
         total += (long)nt[b] * H;
     }
+    pl->shape = choose_shape(p->head_dim, pl->NB, pl->R, p->waves_override, total);
+    pl->shape.fp8 = p->kv_dtype == BLOCKATTN_KV_FP8_E4M3;
     // Workgroups resident per CU, from the kernel's waves per SIMD and its LDS.
     const int waves = pl->shape.row_waves * pl->shape.token_groups;
     const int waves_per_cu = 4 * pl->shape.waves_per_simd;

@@ -891,6 +891,10 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
 // consumed, into a three-slot LDS ring (row-major, padded pitch). One workgroup
 // barrier per tile orders the ring; it waits on LDS traffic only, so the DR tiles
 // of global loads stay in flight across it.
+// With TG token groups the workgroup holds TG such row-wave sets, each with its own
+// ring, taking every TG-th tile of the unit (group g: tiles g, g + TG, ...), so each
+// wave can own two row blocks (half the LDS reads per row of a one-block wave) while
+// two waves still share each SIMD. The groups' softmax states meet in LDS at the end.
 // Pipelined across tiles: while a wave runs the softmax and PV product of tile t, the
 // score MFMAs of tile t + 1 are already issued (its keys sit in the next ring slot), so
 // the matrix cores and the vector ALUs of a SIMD work on different tiles at once.
@@ -898,9 +902,9 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(const KernelArgs a) {
 // would fall past the unit's last tile, or past the tile's last block, go through a
 // buffer resource with no records: the instruction runs (the wait counts stay exact)
 // but reads nothing from memory and returns zeros.
-template <int D, int NBW, bool WINDOWED, bool ALL_ON, int WR, int DR, bool FP8>
-__global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared_kernel(const KernelArgs a) {
-    constexpr int NT = 64 * WR;
+template <int D, int NBW, bool WINDOWED, bool ALL_ON, int WR, int DR, bool FP8, int TG>
+__global__ __launch_bounds__(64 * WR * TG, (D == 64 || NBW == 1 || TG > 1) ? 2 : 1) void shared_kernel(const KernelArgs a) {
+    constexpr int NT = 64 * WR * TG;
     constexpr int EB = FP8 ? 1 : 2;       // bytes per cached element
     constexpr int LE = 16 / EB;           // elements per 16-byte lane load
     constexpr int PL = D / LE;            // lanes per tile row
@@ -919,13 +923,15 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tg = wave / WR, wr = wave - tg * WR;  // token group, row-wave inside it
     const int r16 = lane & 15, quad = lane >> 4;
     trace_point(a, kTrEntry);
     const Unit u = decode_unit<WINDOWED>(a);
     trace_point(a, kTrLength);
     WaveRows<D, NBW, WINDOWED, ALL_ON> w;
-    w.init(a, u, wave * NBW, lane);
-    int* pid_tab = reinterpret_cast<int*>(lds + NSLOT * SLOT);
+    w.init(a, u, wr * NBW, lane);
+    uint16_t* ring = lds + tg * NSLOT * SLOT;  // this token group's ring
+    int* pid_tab = reinterpret_cast<int*>(lds + TG * NSLOT * SLOT);
 
     const int32_t* pt_row = a.page_table + (size_t)u.b * a.stride;
     const int last_page = max(u.NC - 1, 0) >> a.p_shift;
@@ -942,7 +948,7 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
 
     // Key fragments (A operand of S^T = K Q^T) of the tile in ring slot `slot`.
     auto read_k = [&](int slot, bf16x8_t (&kf)[2][KK]) {
-        const uint16_t* kl = lds + slot * SLOT;
+        const uint16_t* kl = ring + slot * SLOT;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -952,7 +958,7 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
     };
     // Value fragments (V^T, transposed from the row-major tile) of the tile in ring slot `slot`.
     auto read_v = [&](int slot, bf16x8_t (&vf)[DB]) {
-        const uint16_t* vrow = lds + slot * SLOT + T * KP + (4 * quad + (r16 >> 2)) * VP + 4 * (r16 & 3);
+        const uint16_t* vrow = ring + slot * SLOT + T * KP + (4 * quad + (r16 >> 2)) * VP + 4 * (r16 & 3);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             const u32x2_t lo = lds_read_tr16(vrow + db * 16);
@@ -984,17 +990,21 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
         }
         __syncthreads();
         if (win == u.ulo) trace_point(a, kTrPages);
-        const int nk = span;
+        // This group's tiles of the window: local tile t is window tile TG * t + tg. Every
+        // group runs the same number of steps (the barriers are shared); a group with one
+        // tile fewer idles through its last step.
+        const int nk = (span - tg + TG - 1) / TG;
+        const int steps = (span + TG - 1) / TG;
 
         // A tile is NBLK blocks of 64 16-byte pieces in four parts (K rows 0-15,
-        // K rows 16-31, V rows 0-15, V rows 16-31) of BP blocks each. Wave w moves
+        // K rows 16-31, V rows 0-15, V rows 16-31) of BP blocks each. Row-wave w moves
         // blocks w, w + WR, ..., so each block's part, page and bases are wave-uniform
         // scalars and a lane's offset inside a block is fixed. A wave's slot past the last
         // block, and every block of a tile past the unit's end, reads through an empty
         // buffer resource (zeros, no memory traffic) and is not stored.
         auto issue = [&](Stage& st, int t) {
             const bool real = t < nk;
-            const int tc = real ? t : nk - 1;
+            const int tc = real ? TG * t + tg : 0;  // window tile (any valid one when not real)
             const int sl0 = __builtin_amdgcn_readfirstlane(pid_tab[2 * tc]);
             const int sl1 = __builtin_amdgcn_readfirstlane(pid_tab[2 * tc + 1]);
             const int t0 = (win + tc) * T;
@@ -1002,7 +1012,7 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
             const size_t slab1 = ((size_t)sl1 << (a.p_shift + kLog2<D>)) + (size_t)(((t0 + 16) & pmask) * D);
 #pragma unroll
             for (int k = 0; k < LPT; ++k) {
-                const int bw = wave + k * WR;
+                const int bw = wr + k * WR;
                 const int b = min(bw, NBLK - 1);
                 const int part = b / BP;
                 const char* base = static_cast<const char*>((part >> 1) ? a.vc : a.kc) +
@@ -1012,12 +1022,12 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
             }
         };
         auto store = [&](const Stage& st, int t, int slot) {
-            const int t0 = (win + t) * T;
+            const int t0 = (win + TG * t + tg) * T;
             const bool tail = t0 + T > u.NC;
-            char* dst = reinterpret_cast<char*>(lds + slot * SLOT);
+            char* dst = reinterpret_cast<char*>(ring + slot * SLOT);
 #pragma unroll
             for (int k = 0; k < LPT; ++k) {
-                const int bw = wave + k * WR;
+                const int bw = wr + k * WR;
                 if (k * WR >= NBLK - (WR - 1) && bw >= NBLK) continue;  // this wave has no block here
                 const int b = bw;
                 const int part = b / BP;
@@ -1068,7 +1078,7 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
             w.scores(kf, s_cur);
         }
         int slot = 0;  // ring slot of tile t
-        for (int tb = 0; tb < nk; tb += DR) {
+        for (int tb = 0; tb < steps; tb += DR) {
 #pragma unroll
             for (int j = 0; j < DR; ++j) {
                 const int t = tb + j;
@@ -1083,7 +1093,7 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
                     w.scores(kf, s_next);
                     bf16x8_t vf[DB];
                     read_v(slot, vf);
-                    w.update(s_cur, vf, (win + t) * T, a.scale_log2, quad);
+                    w.update(s_cur, vf, (win + TG * t + tg) * T, a.scale_log2, quad);
 #pragma unroll
                     for (int n = 0; n < NBW; ++n) {
                         s_cur[n][0] = s_next[n][0];
@@ -1100,8 +1110,8 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
     }
     if (a.k_block != nullptr && u.s == u.S - 1) {
         // The block keys C .. N - 1 (K <= 16 of them) from the dense arrays into ring
-        // slot 0 (rows past K zero), consumed as one more tile at token C by every
-        // row-wave; then the optional append.
+        // slot 0 of token group 0 (rows past K zero), consumed as one more tile at token
+        // C by that group's row-waves; then the optional append.
         __syncthreads();  // every wave is done with the ring
         const size_t rstride = (size_t)a.Hkv * D;
         const size_t b0 = ((size_t)u.b * a.K * a.Hkv + u.hk) * D;
@@ -1115,7 +1125,7 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
         }
         __syncthreads();
         w.hi_cap = u.N;
-        {
+        if (tg == 0) {
             bf16x8_t kf[2][KK];
             read_k(0, kf);
             f32x4_t sb[NBW][2];
@@ -1127,7 +1137,7 @@ __global__ __launch_bounds__(64 * WR, (D == 64 || NBW == 1) ? 2 : 1) void shared
         if (a.append && u.rg == 0) append_block<D, FP8>(a, u);
     }
     if (wave == 0) trace_point(a, kTrLoop);
-    finish_unit(a, u, w, 0, wave, 1, WR, reinterpret_cast<float*>(lds));
+    finish_unit(a, u, w, tg, wr, TG, WR, reinterpret_cast<float*>(lds));
 }
 
 // ---------------------------------------------------------------------------------
@@ -1301,34 +1311,37 @@ hipError_t launch_stream(const KernelShape& s, int units, const KernelArgs& args
 
 // Tiles in flight per lane: about 96 registers of staged loads for a wave alone on
 // its SIMD (D = 128, two row blocks), 64 where two waves share a SIMD, at most 8.
-constexpr int shared_depth(int D, int NBW, int WR, bool FP8) {
+// Two row blocks with two waves per SIMD (token groups) leave room for two.
+constexpr int shared_depth(int D, int NBW, int WR, bool FP8, int TG) {
     const int lpt = ((FP8 ? D / 16 : D / 8) + WR - 1) / WR;  // 1-KiB blocks per wave per tile
-    const int dr = ((D == 128 && NBW == 2) ? 24 : 16) / lpt;
+    const int dr = (D == 128 && NBW == 2 && TG > 1) ? 2 : ((D == 128 && NBW == 2) ? 24 : 16) / lpt;
     return dr < 2 ? 2 : (dr > 8 ? 8 : dr);
 }
 
-template <int D, int NBW, int WR, bool W, bool ALL_ON, bool FP8>
+template <int D, int NBW, int WR, bool W, bool ALL_ON, bool FP8, int TG>
 hipError_t launch_shared(const KernelShape& s, int units, const KernelArgs& args, hipStream_t stream) {
     static LdsGrant grant;
-    return launch_with_lds(shared_kernel<D, NBW, W, ALL_ON, WR, shared_depth(D, NBW, WR, FP8), FP8>, units, 64 * WR,
-                           s.lds_bytes, args, stream, grant);
+    return launch_with_lds(shared_kernel<D, NBW, W, ALL_ON, WR, shared_depth(D, NBW, WR, FP8, TG), FP8, TG>, units,
+                           64 * WR * TG, s.lds_bytes, args, stream, grant);
 }
 
 template <bool W, bool FP8>
 hipError_t dispatch(const KernelShape& s, int units, const KernelArgs& args, hipStream_t stream) {
     if (s.shared) {
-#define BA_SHARED(D_, NBW_, WR_)                                                                        \
-    if (s.head_dim == D_ && s.nbw == NBW_ && s.row_waves == WR_)                                        \
-        return s.all_on ? launch_shared<D_, NBW_, WR_, W, true, FP8>(s, units, args, stream)            \
-                        : launch_shared<D_, NBW_, WR_, W, false, FP8>(s, units, args, stream);
+#define BA_SHARED(D_, NBW_, WR_, TG_)                                                                   \
+    if (s.head_dim == D_ && s.nbw == NBW_ && s.row_waves == WR_ && s.token_groups == TG_)               \
+        return s.all_on ? launch_shared<D_, NBW_, WR_, W, true, FP8, TG_>(s, units, args, stream)       \
+                        : launch_shared<D_, NBW_, WR_, W, false, FP8, TG_>(s, units, args, stream);
 #define BA_SHARED1(D_, WR_)                                                                             \
-    if (s.head_dim == D_ && s.nbw == 1 && s.row_waves == WR_) return launch_shared<D_, 1, WR_, W, true, FP8>(s, units, args, stream);
-        BA_SHARED(64, 2, 2)
-        BA_SHARED(64, 2, 3)
-        BA_SHARED(64, 2, 4)
-        BA_SHARED(128, 2, 2)
-        BA_SHARED(128, 2, 3)
-        BA_SHARED(128, 2, 4)
+    if (s.head_dim == D_ && s.nbw == 1 && s.row_waves == WR_ && s.token_groups == 1)                    \
+        return launch_shared<D_, 1, WR_, W, true, FP8, 1>(s, units, args, stream);
+        BA_SHARED(64, 2, 2, 1)
+        BA_SHARED(64, 2, 3, 1)
+        BA_SHARED(64, 2, 4, 1)
+        BA_SHARED(128, 2, 2, 1)
+        BA_SHARED(128, 2, 3, 1)
+        BA_SHARED(128, 2, 4, 1)
+        BA_SHARED(128, 2, 4, 2)
         BA_SHARED1(128, 3)
         BA_SHARED1(128, 4)
         BA_SHARED1(128, 5)

@@ -40,8 +40,9 @@ size_t attention_lds_bytes(const KernelShape& s, int R) {
     const int D = s.head_dim;
     if (s.shared) {
         const size_t pitches = D == 64 ? kKPitch<64> + kVPitch<64> : kKPitch<128> + kVPitch<128>;
-        const size_t ring = (size_t)3 * kTileTokens * pitches * sizeof(uint16_t) + 2 * kPidWindow * sizeof(int);
-        const size_t epi = epilogue_floats(D, s.row_waves * s.nbw, 1) * sizeof(float);
+        const size_t ring = (size_t)s.token_groups * 3 * kTileTokens * pitches * sizeof(uint16_t) +
+                            2 * kPidWindow * sizeof(int);
+        const size_t epi = epilogue_floats(D, s.row_waves * s.nbw, s.token_groups) * sizeof(float);
         return ring > epi ? ring : epi;
     }
     const size_t vpitch = D == 64 ? kVPitch<64> : kVPitch<128>;

@@ -66,13 +66,32 @@ def test_waves_override():
     assert plan_info(params(waves_override=8), [5000, 5000])["token_groups"] == 8
     assert plan_info(params(waves_override=1), [5000, 5000])["waves_per_unit"] == 1
     w = dict(head_dim=128, page_size=64, num_q_heads=16, num_kv_heads=1, window_left=4096, block_size=7)
-    # R = 112 at D = 128 shares tiles: waves per workgroup = rows per wave choice
-    info = plan_info(params(**w, waves_override=8), [8199, 8199])
+    # R = 112 at D = 128 shares tiles: waves per workgroup = rows per wave choice, and a count
+    # above the seven row blocks selects two token groups of four two-block waves
+    info = plan_info(params(**w, waves_override=7), [8199, 8199])
     assert info["row_waves"] == 7 and info["token_groups"] == 1 and info["shared_tiles"] == 1
+    info = plan_info(params(**w, waves_override=8), [8199, 8199])
+    assert info["row_waves"] == 4 and info["token_groups"] == 2 and info["waves_per_unit"] == 8
     info = plan_info(params(**w, waves_override=4), [8199, 8199])
     assert info["row_waves"] == 4 and info["waves_per_unit"] == 4
     info = plan_info(params(**w, waves_override=1), [8199, 8199])
     assert info["row_waves"] == 4  # at most two row blocks per wave
+
+
+def test_two_token_groups_for_many_row_blocks_and_tiles():
+    """Seven or eight row blocks at D = 128 run as two token groups of four two-block waves
+    once the batch holds at least 8 tiles per CU (2048 tiles); smaller batches keep one
+    group of one-block waves."""
+    w = dict(head_dim=128, page_size=64, num_q_heads=16, num_kv_heads=1, window_left=4096, window_right=-1)
+    for K, blocks in ((7, 7), (8, 8)):
+        n = 16384 + K  # 129 tiles of the window per request
+        small = plan_info(params(**w, block_size=K, batch=15), [n] * 15)  # 1935 tiles
+        big = plan_info(params(**w, block_size=K, batch=16), [n] * 16)    # 2064 tiles
+        assert small["token_groups"] == 1 and small["row_waves"] == blocks
+        assert big["token_groups"] == 2 and big["row_waves"] == 4 and big["waves_per_unit"] == 8
+    # five and six blocks keep one group at any size
+    info = plan_info(params(**w, block_size=5, batch=64), [16389] * 64)
+    assert info["token_groups"] == 1 and info["row_waves"] == 5
 
 
 def test_tile_kernel_choice():
@@ -96,7 +115,10 @@ def test_more_than_128_rows_run_as_row_groups():
     two = plan_info(params(**w, block_size=16, num_q_heads=16, num_kv_heads=1), [4000, 4000])  # R = 256
     three = plan_info(params(**w, block_size=9, num_q_heads=32, num_kv_heads=2), [4000, 4000])  # R = 144
     assert one["row_groups"] == 1 and two["row_groups"] == 2 and three["row_groups"] == 2
-    assert two["row_waves"] == 8 and three["row_waves"] == 5  # 144 rows: two groups of five row blocks
+    # 128-row groups of eight one-block waves (a small batch); 144 rows: two row groups of
+    # five row blocks
+    assert two["row_waves"] == 8 and two["token_groups"] == 1
+    assert three["row_waves"] == 5 and three["token_groups"] == 1
     # every row group gets the same split count, so the units scale with the groups
     forced = [plan_info(params(**w, block_size=k, num_q_heads=16, num_kv_heads=1, splits_override=3), [4000, 4000])
               for k in (8, 16)]

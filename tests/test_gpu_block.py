@@ -58,9 +58,9 @@ def random_block(c, seed, scale=1.0):
     return mk(), mk()
 
 
-def run_block(dc, kb, vb, *, append, splits=0):
+def run_block(dc, kb, vb, *, append, splits=0, waves=0):
     c = dc.inputs.case
-    prm = H.params_for(dc, splits=splits)
+    prm = H.params_for(dc, splits=splits, waves=waves)
     lens = dc.inputs.seq_lens
     nbytes = ba.blockattn_workspace_size(prm, lens)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
@@ -162,6 +162,36 @@ def test_fused_append_stores_the_encoded_block(idx, kw):
     out2, lse2, _ = H.run(H.upload(after))
     ref2_out, ref2_lse = oracle.attention_case(after)
     H.compare(out2, lse2, ref2_out, ref2_lse, label=f"after append bk{idx}")
+
+
+# Seven and eight row blocks at D = 128 as two token groups (waves_override 8 or a large batch):
+# the block tile is consumed by the first group only, the append by every wave.
+TWO_GROUPS = [
+    (30, dict(batch=2, K=7, hq=16, hkv=1, D=128, P=64, ctx=2500, wl=1000, wr=-1), 8, False),
+    (31, dict(fp8=True, batch=3, K=7, hq=16, hkv=1, D=128, P=32, ctx_range=(0, 900)), 8, True),
+    (32, dict(batch=2, K=7, hq=32, hkv=2, D=128, P=64, ctx=1300, wl=700, wr=2), 8, True),
+    (33, dict(batch=16, K=8, hq=16, hkv=1, D=128, P=64, ctx=4100, wl=4096, wr=-1), 0, False),
+]
+
+
+@pytest.mark.parametrize("idx,kw,waves,append", TWO_GROUPS, ids=[f"bk{i}" for i, *_ in TWO_GROUPS])
+def test_dense_block_and_append_with_two_token_groups(idx, kw, waves, append):
+    c = bcase(idx, **kw)
+    inp = synth.make_inputs(c)
+    poison_block_slots(inp)
+    kb, vb = random_block(c, 200 + idx, scale=2.0)
+    want_k, want_v = expected_append(inp, kb, vb) if append else (inp.k_pool, inp.v_pool)
+    dc = H.upload(inp)
+    prm = H.params_for(dc, waves=waves)
+    info = ba.blockattn_plan(prm, inp.seq_lens, None).info()
+    assert info["token_groups"] == 2 and info["row_waves"] == 4
+    out, lse = run_block(dc, kb, vb, append=append, waves=waves)
+    ref_out, ref_lse = oracle.attention_case(inp, k_block=kb, v_block=vb)
+    H.compare(out, lse, ref_out, ref_lse, label=f"two groups bk{idx}")
+    got_k = dc.k.view(torch.uint8).cpu().numpy().view(want_k.dtype).reshape(want_k.shape)
+    got_v = dc.v.view(torch.uint8).cpu().numpy().view(want_v.dtype).reshape(want_v.shape)
+    np.testing.assert_array_equal(got_k, want_k)
+    np.testing.assert_array_equal(got_v, want_v)
 
 
 def test_append_encoding_of_special_values():

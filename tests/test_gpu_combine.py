@@ -36,6 +36,8 @@ CASES = [
     (7, dict(fp8=True, batch=2, ctx=7000), 12),                            # fp8 pools
     (8, dict(batch=1, ctx=20000), 125),                                    # many splits
     (9, dict(K=1, hq=8, hkv=2, ctx=2500, wl=700, wr=-1), 7),               # one query: windowed decode
+    # R = 112 over 2064 tiles: two token groups of the shared-tile kernel
+    (10, dict(batch=16, K=7, hq=16, hkv=1, D=128, P=64, ctx=4200, wl=4096, wr=-1), 3),
 ]
 
 

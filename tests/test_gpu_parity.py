@@ -94,28 +94,52 @@ def test_split_invariance(splits):
     assert np.abs(out - base).max() <= 4 * H.ulp_bf16(float(np.abs(base).max()))
 
 
+@pytest.mark.parametrize("waves,groups", [(0, 1), (8, 2)])
 @pytest.mark.parametrize("splits", [1, 3, 1000])
-def test_split_invariance_shared_tiles(splits):
+def test_split_invariance_shared_tiles(splits, waves, groups):
     c = case(36, batch=2, K=7, hq=16, hkv=1, D=128, P=64, ctx=3000, wl=2000, wr=-1)
     inp = synth.make_inputs(c)
     dc = H.upload(inp)
     ref_out, ref_lse = oracle.attention_case(inp)
-    out, lse, info = H.run(dc, splits=splits)
-    assert info["shared_tiles"] == 1 and info["row_waves"] == 7
-    H.compare(out, lse, ref_out, ref_lse, label=f"shared splits={splits}")
-    base, _, _ = H.run(dc, splits=1)
+    out, lse, info = H.run(dc, splits=splits, waves=waves)
+    assert info["shared_tiles"] == 1 and info["token_groups"] == groups
+    assert info["row_waves"] == (7 if groups == 1 else 4)
+    H.compare(out, lse, ref_out, ref_lse, label=f"shared splits={splits} groups={groups}")
+    base, _, _ = H.run(dc, splits=1, waves=waves)
     assert np.abs(out - base).max() <= 4 * H.ulp_bf16(float(np.abs(base).max()))
 
 
-@pytest.mark.parametrize("K,waves,row_waves", [(7, 4, 4), (5, 3, 3), (3, 3, 3), (3, 2, 2), (3, 0, 3), (7, 8, 7)])
-def test_rows_per_wave_variants(K, waves, row_waves):
-    """Every row-blocks-per-wave choice of the shared-tile kernel at D = 128 meets the bar."""
+@pytest.mark.parametrize("K,waves,row_waves,groups",
+                         [(7, 4, 4, 1), (5, 3, 3, 1), (3, 3, 3, 1), (3, 2, 2, 1), (3, 0, 3, 1), (7, 7, 7, 1),
+                          (7, 8, 4, 2), (7, 0, 7, 1), (8, 0, 8, 1)])
+def test_rows_per_wave_variants(K, waves, row_waves, groups):
+    """Every row-blocks-per-wave choice of the shared-tile kernel at D = 128 meets the bar,
+    with one token group or two (seven or eight row blocks)."""
     c = case(37 + K, batch=2, K=K, hq=16, hkv=1, D=128, P=64, ctx=2500, wl=1000, wr=-1)
     inp = synth.make_inputs(c)
     ref_out, ref_lse = oracle.attention_case(inp)
     out, lse, info = H.run(H.upload(inp), waves=waves)
-    assert info["shared_tiles"] == 1 and info["row_waves"] == row_waves
+    assert info["shared_tiles"] == 1 and info["row_waves"] == row_waves and info["token_groups"] == groups
     H.compare(out, lse, ref_out, ref_lse, label=f"K={K} waves={waves}")
+
+
+# Two token groups (seven or eight row blocks at D = 128): odd and even tile counts per unit (the
+# second group idles through the last step of an odd one), forced splits, the all-on eight-block
+# form, and the size rule that picks them without an override.
+TWO_GROUPS = [
+    (90, dict(batch=3, K=7, hq=16, hkv=1, D=128, P=32, ctx_range=(0, 2000)), 8),              # unwindowed, ragged
+    (91, dict(batch=2, K=7, hq=32, hkv=2, D=128, P=128, ctx=3333, wl=1500, wr=3), 8),         # W_r = 3
+    (92, dict(batch=2, K=7, hq=16, hkv=1, D=128, P=16, ctx_range=(100, 2500), wl=64, wr=-1), 8),  # short window
+    (93, dict(batch=16, K=7, hq=16, hkv=1, D=128, P=64, ctx=4200, wl=4096, wr=-1), 0),        # 2064 tiles: default
+    (94, dict(batch=3, K=8, hq=64, hkv=4, D=128, P=64, ctx_range=(5000, 9000)), 0),          # all on, default
+]
+
+
+@pytest.mark.parametrize("idx,kw,waves", TWO_GROUPS, ids=[f"groups_{i}" for i, *_ in TWO_GROUPS])
+def test_two_token_groups(idx, kw, waves):
+    _, _, info = check_full(case(idx, **kw), f"groups_{idx}", waves=waves)
+    assert info["token_groups"] == 2 and info["row_waves"] == 4
+    check_full(case(idx, **kw), f"groups_{idx} splits=3", waves=waves, splits=3)
 
 
 def test_empty_splits_from_shorter_live_lengths():
