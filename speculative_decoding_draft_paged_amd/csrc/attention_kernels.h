@@ -287,13 +287,15 @@ struct WaveRows {
         hi_cap = u.NC;
     }
 
-    // Scores of one tile for every owned row block.
+    // Scores of one tile for every owned row block. ALL: also for a block with no live
+    // rows (zero queries; its state is never stored), so the code has no branch.
+    template <bool ALL = false>
     __device__ __forceinline__ void scores(const bf16x8_t (&kf)[2][KK], f32x4_t (&s)[NBW][2]) const {
 #pragma unroll
         for (int n = 0; n < NBW; ++n) {
             s[n][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             s[n][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            if (ALL_ON || on[n]) {
+            if (ALL_ON || ALL || on[n]) {
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
@@ -304,23 +306,23 @@ struct WaveRows {
         }
     }
 
-    // Online softmax update and O^T += V^T P^T for one tile starting at token t0.
+    // Online softmax update and O^T += V^T P^T for one tile starting at token t0, in
+    // two parts: prep (masking, exponent arguments, the rare move of the reference)
+    // and apply (probabilities, row sums and the PV product), so a caller can issue
+    // other work between them.
     // m[n] is the reference maximum (log2 units) the row sums are kept relative to.
     // It only moves when a score exceeds it by more than kRescaleSlack, so the
     // accumulator rescale is rare and probabilities stay below 2^kRescaleSlack
     // (exact in fp32 and representable in bf16). The softmax scale is folded into
     // the exponent's FMA.
-    // PMUL: the tile's values are in other units than the accumulator's; each
-    // probability is multiplied by pmul (after it joins the row sum) before its bf16
-    // rounding for the P V product.
-    template <bool PMUL = false>
-    __device__ __forceinline__ void update(const f32x4_t (&s)[NBW][2], const bf16x8_t (&vf)[DB], int t0, float scale,
-                                           int quad, float pmul = 1.f) {
+    template <bool ALL = false>
+    __device__ __forceinline__ void prep(const f32x4_t (&s)[NBW][2], int t0, float scale, int quad,
+                                         float (&y)[NBW][8]) {
         constexpr float kRescaleSlack = 8.f;
         const bool edge = (t0 < lo_max) || (t0 + T - 1 > hi_min) || (t0 + T > hi_cap);
 #pragma unroll
         for (int n = 0; n < NBW; ++n) {
-            if (!ALL_ON && !on[n]) continue;
+            if (!ALL_ON && !ALL && !on[n]) continue;
             float x[8];
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
@@ -340,10 +342,10 @@ struct WaveRows {
             // four-lane maximum is needed only when an argument passes the gate; a row's
             // maximum is at least each of its lanes' maxima, so when no lane of the wave
             // passes (the common case after a row's first tile) no row needs a rescale.
-            float y[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) y[k] = fmaf(x[k], scale, neg_m[n]);
-            const float ymax = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])), fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
+            for (int k = 0; k < 8; ++k) y[n][k] = fmaf(x[k], scale, neg_m[n]);
+            const float ymax = fmaxf(fmaxf(fmaxf(y[n][0], y[n][1]), fmaxf(y[n][2], y[n][3])),
+                                     fmaxf(fmaxf(y[n][4], y[n][5]), fmaxf(y[n][6], y[n][7])));
             if (__builtin_amdgcn_ballot_w64(ymax > gate[n]) != 0) {
                 const float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
                 const float mxs = quad_max(mx) * scale;  // scale > 0, so the maximum commutes with it
@@ -357,13 +359,24 @@ struct WaveRows {
                     gate[n] = kRescaleSlack;
                 }
 #pragma unroll
-                for (int k = 0; k < 8; ++k) y[k] = fmaf(x[k], scale, neg_m[n]);
+                for (int k = 0; k < 8; ++k) y[n][k] = fmaf(x[k], scale, neg_m[n]);
             }
+        }
+    }
+
+    // PMUL: the tile's values are in other units than the accumulator's; each
+    // probability is multiplied by pmul (after it joins the row sum) before its bf16
+    // rounding for the P V product.
+    template <bool PMUL = false, bool ALL = false>
+    __device__ __forceinline__ void apply(const float (&y)[NBW][8], const bf16x8_t (&vf)[DB], float pmul = 1.f) {
+#pragma unroll
+        for (int n = 0; n < NBW; ++n) {
+            if (!ALL_ON && !ALL && !on[n]) continue;
             bf16x8_t pb;
             float p[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                p[k] = fast_exp2(y[k]);
+                p[k] = fast_exp2(y[n][k]);
                 if constexpr (PMUL)
                     pb[k] = (__bf16)(p[k] * pmul);
                 else
@@ -374,6 +387,14 @@ struct WaveRows {
             for (int db = 0; db < DB; ++db)
                 acc[n][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pb, acc[n][db], 0, 0, 0);
         }
+    }
+
+    template <bool PMUL = false>
+    __device__ __forceinline__ void update(const f32x4_t (&s)[NBW][2], const bf16x8_t (&vf)[DB], int t0, float scale,
+                                           int quad, float pmul = 1.f) {
+        float y[NBW][8];
+        prep(s, t0, scale, quad, y);
+        apply<PMUL>(y, vf, pmul);
     }
 };
 
@@ -1085,15 +1106,18 @@ __global__ __launch_bounds__(64 * WR * TG, (D == 64 || NBW == 1 || TG > 1) ? 2 :
                 const int slot1 = slot == NSLOT - 1 ? 0 : slot + 1;    // tile t + 1
                 const int slot2 = slot1 == NSLOT - 1 ? 0 : slot1 + 1;  // tile t + 2 (held tile t - 1)
                 if (t < nk) {
-                    // scores of tile t + 1 first (past the end: zeros, unused), then the
-                    // softmax and PV product of tile t
+                    // exponent arguments of tile t, then in one straight run the scores of
+                    // tile t + 1 (past the end: zeros, unused) and the probabilities and PV
+                    // product of tile t (a block with no live rows computes too: no branch)
+                    float y[NBW][8];
+                    w.template prep<true>(s_cur, (win + TG * t + tg) * T, a.scale_log2, quad, y);
                     f32x4_t s_next[NBW][2];
                     bf16x8_t kf[2][KK];
                     read_k(slot1, kf);
-                    w.scores(kf, s_next);
                     bf16x8_t vf[DB];
                     read_v(slot, vf);
-                    w.update(s_cur, vf, (win + TG * t + tg) * T, a.scale_log2, quad);
+                    w.template scores<true>(kf, s_next);
+                    w.template apply<false, true>(y, vf);
 #pragma unroll
                     for (int n = 0; n < NBW; ++n) {
                         s_cur[n][0] = s_next[n][0];
