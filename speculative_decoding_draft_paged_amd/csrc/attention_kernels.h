@@ -315,28 +315,29 @@ struct WaveRows {
     // accumulator rescale is rare and probabilities stay below 2^kRescaleSlack
     // (exact in fp32 and representable in bf16). The softmax scale is folded into
     // the exponent's FMA.
+    // The scores are masked in place (s is consumed).
     template <bool ALL = false>
-    __device__ __forceinline__ void prep(const f32x4_t (&s)[NBW][2], int t0, float scale, int quad,
-                                         float (&y)[NBW][8]) {
+    __device__ __forceinline__ void prep(f32x4_t (&s)[NBW][2], int t0, float scale, int quad, float (&y)[NBW][8]) {
         constexpr float kRescaleSlack = 8.f;
         const bool edge = (t0 < lo_max) || (t0 + T - 1 > hi_min) || (t0 + T > hi_cap);
 #pragma unroll
         for (int n = 0; n < NBW; ++n) {
             if (!ALL_ON && !ALL && !on[n]) continue;
-            float x[8];
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) x[mb * 4 + j] = s[n][mb][j];
             if (edge) {
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int tok = t0 + mb * 16 + quad * 4 + j;
-                        if (tok < row_lo[n] || tok > row_hi[n] || tok >= hi_cap) x[mb * 4 + j] = kNegInf;
+                        const bool out = tok < row_lo[n] || tok > row_hi[n] || tok >= hi_cap;
+                        s[n][mb][j] = out ? kNegInf : s[n][mb][j];
                     }
             }
+            float x[8];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) x[mb * 4 + j] = s[n][mb][j];
             // Exponent arguments against the current reference. They are arithmetic
             // results, so their maximum needs no operand canonicalisation. The row's
             // four-lane maximum is needed only when an argument passes the gate; a row's
@@ -390,7 +391,7 @@ struct WaveRows {
     }
 
     template <bool PMUL = false>
-    __device__ __forceinline__ void update(const f32x4_t (&s)[NBW][2], const bf16x8_t (&vf)[DB], int t0, float scale,
+    __device__ __forceinline__ void update(f32x4_t (&s)[NBW][2], const bf16x8_t (&vf)[DB], int t0, float scale,
                                            int quad, float pmul = 1.f) {
         float y[NBW][8];
         prep(s, t0, scale, quad, y);
@@ -933,6 +934,9 @@ __global__ __launch_bounds__(64 * WR * TG, (D == 64 || NBW == 1 || TG > 1) ? 2 :
     constexpr int BP = NBLK / 4;          // blocks per 16-row half of K or V
     constexpr int RPB = 64 * LE / D;      // tile rows per block
     constexpr int LPT = (NBLK + WR - 1) / WR;
+    // Four row-waves: wave w moves the BP blocks of part w (one 16-row half of K or V,
+    // contiguous in its page), through one buffer resource per tile.
+    constexpr bool PPW = WR * BP == NBLK;
     constexpr int KP = kKPitch<D>;        // padded row pitch (bf16) of the K tile in LDS
     constexpr int VP = kVPitch<D>;        // and of the V tile
     constexpr int SLOT = T * (KP + VP);   // bf16 elements per ring slot: K tile, then V tile
@@ -962,6 +966,7 @@ __global__ __launch_bounds__(64 * WR * TG, (D == 64 || NBW == 1 || TG > 1) ? 2 :
     const uint32_t lane_goff = (uint32_t)(lrow * D + lcol) * EB;  // bytes, in the cache
     const uint32_t lane_koff = (uint32_t)(lrow * KP + lcol) * 2;  // bytes, in the K tile
     const uint32_t lane_voff = (uint32_t)(lrow * VP + lcol) * 2;  // bytes, in the V tile
+    const void* pool_w = (wr >> 1) ? a.vc : a.kc;                 // the pool of this wave's part (one part per wave)
 
     struct Stage {
         u32x4_t c[LPT];
@@ -1026,6 +1031,25 @@ __global__ __launch_bounds__(64 * WR * TG, (D == 64 || NBW == 1 || TG > 1) ? 2 :
         auto issue = [&](Stage& st, int t) {
             const bool real = t < nk;
             const int tc = real ? TG * t + tg : 0;  // window tile (any valid one when not real)
+            if constexpr (PPW) {
+                const int h = wr & 1;  // the part's 16-token half of the tile
+                const int sl = __builtin_amdgcn_readfirstlane(pid_tab[2 * tc + h]);
+                const int t0 = (win + tc) * T + 16 * h;
+                const size_t slab = ((size_t)sl << (a.p_shift + kLog2<D>)) + (size_t)((t0 & pmask) * D);
+                // The resource ends at the last cached row: rows past it read as zeros (a
+                // V row there must not be a stale NaN; a K row there is masked anyway).
+                const int rows = real ? min(16, max(0, u.NC - t0)) : 0;
+                const uint64_t addr = reinterpret_cast<uint64_t>(pool_w) + slab * EB;
+                const char* base = reinterpret_cast<const char*>(
+                    ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32)) << 32) |
+                    (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)addr));
+                // (scalar operands: a resource built from vector registers needs a per-lane loop)
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, __builtin_amdgcn_readfirstlane(rows * D * EB));
+#pragma unroll
+                for (int k = 0; k < LPT; ++k)
+                    st.c[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane_goff + k * 64 * 16, 0, kCachePolicyStream);
+                return;
+            }
             const int sl0 = __builtin_amdgcn_readfirstlane(pid_tab[2 * tc]);
             const int sl1 = __builtin_amdgcn_readfirstlane(pid_tab[2 * tc + 1]);
             const int t0 = (win + tc) * T;
@@ -1042,10 +1066,39 @@ __global__ __launch_bounds__(64 * WR * TG, (D == 64 || NBW == 1 || TG > 1) ? 2 :
                 st.c[k] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(base, bytes), lane_goff, 0, kCachePolicyStream);
             }
         };
-        auto store = [&](const Stage& st, int t, int slot) {
+        auto store = [&](Stage& st, int t, int slot) {
             const int t0 = (win + TG * t + tg) * T;
             const bool tail = t0 + T > u.NC;
             char* dst = reinterpret_cast<char*>(ring + slot * SLOT);
+            if constexpr (PPW) {
+                // rows past the cached keys were loaded as zeros (the resource ends there)
+                (void)tail;
+                const int row_h = (wr & 1) * 16;  // first tile row of the wave's part
+                if (wr >> 1) {
+                    char* vd = dst + (T * KP + row_h * VP) * 2 + lane_voff;
+#pragma unroll
+                    for (int k = 0; k < LPT; ++k) {
+                        if constexpr (FP8) {
+                            *(u32x4_t*)(vd + k * RPB * VP * 2) = widen8(u32x2_t{st.c[k].x, st.c[k].y});
+                            *(u32x4_t*)(vd + k * RPB * VP * 2 + 16) = widen8(u32x2_t{st.c[k].z, st.c[k].w});
+                        } else {
+                            *(u32x4_t*)(vd + k * RPB * VP * 2) = st.c[k];
+                        }
+                    }
+                } else {
+                    char* kd = dst + row_h * KP * 2 + lane_koff;
+#pragma unroll
+                    for (int k = 0; k < LPT; ++k) {
+                        if constexpr (FP8) {
+                            *(u32x4_t*)(kd + k * RPB * KP * 2) = widen8(u32x2_t{st.c[k].x, st.c[k].y});
+                            *(u32x4_t*)(kd + k * RPB * KP * 2 + 16) = widen8(u32x2_t{st.c[k].z, st.c[k].w});
+                        } else {
+                            *(u32x4_t*)(kd + k * RPB * KP * 2) = st.c[k];
+                        }
+                    }
+                }
+                return;
+            }
 #pragma unroll
             for (int k = 0; k < LPT; ++k) {
                 const int bw = wr + k * WR;
@@ -1092,11 +1145,13 @@ __global__ __launch_bounds__(64 * WR * TG, (D == 64 || NBW == 1 || TG > 1) ? 2 :
         issue(st[1], DR + 1);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
-        f32x4_t s_cur[NBW][2];
+        // Scores of tiles t and t + 1 in two buffers that swap roles every tile (no copy
+        // when DR is even; an odd DR copies the next into the current).
+        f32x4_t sbuf[2][NBW][2];
         {
             bf16x8_t kf[2][KK];
             read_k(0, kf);
-            w.scores(kf, s_cur);
+            w.scores(kf, sbuf[0]);
         }
         int slot = 0;  // ring slot of tile t
         for (int tb = 0; tb < steps; tb += DR) {
@@ -1105,23 +1160,27 @@ __global__ __launch_bounds__(64 * WR * TG, (D == 64 || NBW == 1 || TG > 1) ? 2 :
                 const int t = tb + j;
                 const int slot1 = slot == NSLOT - 1 ? 0 : slot + 1;    // tile t + 1
                 const int slot2 = slot1 == NSLOT - 1 ? 0 : slot1 + 1;  // tile t + 2 (held tile t - 1)
+                constexpr bool kSwap = DR % 2 == 0;
+                f32x4_t(&s_cur)[NBW][2] = sbuf[kSwap ? (j & 1) : 0];
+                f32x4_t(&s_next)[NBW][2] = sbuf[kSwap ? ((j + 1) & 1) : 1];
                 if (t < nk) {
                     // exponent arguments of tile t, then in one straight run the scores of
                     // tile t + 1 (past the end: zeros, unused) and the probabilities and PV
                     // product of tile t (a block with no live rows computes too: no branch)
                     float y[NBW][8];
                     w.template prep<true>(s_cur, (win + TG * t + tg) * T, a.scale_log2, quad, y);
-                    f32x4_t s_next[NBW][2];
                     bf16x8_t kf[2][KK];
                     read_k(slot1, kf);
                     bf16x8_t vf[DB];
                     read_v(slot, vf);
                     w.template scores<true>(kf, s_next);
                     w.template apply<false, true>(y, vf);
+                    if constexpr (!kSwap) {
 #pragma unroll
-                    for (int n = 0; n < NBW; ++n) {
-                        s_cur[n][0] = s_next[n][0];
-                        s_cur[n][1] = s_next[n][1];
+                        for (int n = 0; n < NBW; ++n) {
+                            s_cur[n][0] = s_next[n][0];
+                            s_cur[n][1] = s_next[n][1];
+                        }
                     }
                 }
                 store(st[(j + 2) % DR], t + 2, slot2);
