@@ -323,14 +323,14 @@ struct WaveRows {
 #pragma unroll
         for (int n = 0; n < NBW; ++n) {
             if (!ALL_ON && !ALL && !on[n]) continue;
-            if (edge) {
+            if (__builtin_expect(edge, 0)) {  // a tile at the window's edges (rare): mask in place
+                const int lo = row_lo[n], hi = min(row_hi[n], hi_cap - 1);
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int tok = t0 + mb * 16 + quad * 4 + j;
-                        const bool out = tok < row_lo[n] || tok > row_hi[n] || tok >= hi_cap;
-                        s[n][mb][j] = out ? kNegInf : s[n][mb][j];
+                        s[n][mb][j] = (tok < lo || tok > hi) ? kNegInf : s[n][mb][j];
                     }
             }
             float x[8];
@@ -1038,7 +1038,7 @@ __global__ __launch_bounds__(64 * WR * TG, (D == 64 || NBW == 1 || TG > 1) ? 2 :
                 const size_t slab = ((size_t)sl << (a.p_shift + kLog2<D>)) + (size_t)((t0 & pmask) * D);
                 // The resource ends at the last cached row: rows past it read as zeros (a
                 // V row there must not be a stale NaN; a K row there is masked anyway).
-                const int rows = real ? min(16, max(0, u.NC - t0)) : 0;
+                const int rows = real ? max(0, u.NC - t0) : 0;  // the loads touch only the part's BP KiB
                 const uint64_t addr = reinterpret_cast<uint64_t>(pool_w) + slab * EB;
                 const char* base = reinterpret_cast<const char*>(
                     ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32)) << 32) |
@@ -1060,19 +1060,20 @@ __global__ __launch_bounds__(64 * WR * TG, (D == 64 || NBW == 1 || TG > 1) ? 2 :
                 const int bw = wr + k * WR;
                 const int b = min(bw, NBLK - 1);
                 const int part = b / BP;
+                const int row0 = (part & 1) * 16 + (b % BP) * RPB;  // first tile row of the block
                 const char* base = static_cast<const char*>((part >> 1) ? a.vc : a.kc) +
                                    (((part & 1) ? slab1 : slab0) + (size_t)(b % BP) * RPB * D) * EB;
-                const int bytes = (real && bw < NBLK) ? 64 * 16 : 0;
-                st.c[k] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(base, bytes), lane_goff, 0, kCachePolicyStream);
+                // the resource ends at the last cached row: rows past it read as zeros (the
+                // loads touch only the block's own 1 KiB, so a longer resource is harmless)
+                const int rows = (real && bw < NBLK) ? max(0, u.NC - (t0 + row0)) : 0;
+                st.c[k] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(base, rows * D * EB), lane_goff, 0,
+                                                                kCachePolicyStream);
             }
         };
-        auto store = [&](Stage& st, int t, int slot) {
-            const int t0 = (win + TG * t + tg) * T;
-            const bool tail = t0 + T > u.NC;
+        auto store = [&](Stage& st, int slot) {
             char* dst = reinterpret_cast<char*>(ring + slot * SLOT);
             if constexpr (PPW) {
                 // rows past the cached keys were loaded as zeros (the resource ends there)
-                (void)tail;
                 const int row_h = (wr & 1) * 16;  // first tile row of the wave's part
                 if (wr >> 1) {
                     char* vd = dst + (T * KP + row_h * VP) * 2 + lane_voff;
@@ -1106,24 +1107,13 @@ __global__ __launch_bounds__(64 * WR * TG, (D == 64 || NBW == 1 || TG > 1) ? 2 :
                 const int b = bw;
                 const int part = b / BP;
                 const int row0 = (part & 1) * 16 + (b % BP) * RPB;  // first tile row of the block
-                // the lane's LE elements as bf16: one 16-byte piece, or two for fp8
-                u32x4_t v0, v1;
+                // rows past the cached keys were loaded as zeros (the block's resource ends there)
+                char* d = dst + ((part >> 1) ? (T * KP + row0 * VP) * 2 + lane_voff : row0 * KP * 2 + lane_koff);
                 if constexpr (FP8) {
-                    v0 = widen8(u32x2_t{st.c[k].x, st.c[k].y});
-                    v1 = widen8(u32x2_t{st.c[k].z, st.c[k].w});
+                    *(u32x4_t*)d = widen8(u32x2_t{st.c[k].x, st.c[k].y});
+                    *(u32x4_t*)(d + 16) = widen8(u32x2_t{st.c[k].z, st.c[k].w});
                 } else {
-                    v0 = st.c[k];
-                }
-                if (part >> 1) {
-                    // V rows past the sequence end become zeros (stale slots may hold NaN)
-                    if (tail && t0 + row0 + lrow >= u.NC) v0 = v1 = u32x4_t{0u, 0u, 0u, 0u};
-                    char* vd = dst + (T * KP + row0 * VP) * 2 + lane_voff;
-                    *(u32x4_t*)vd = v0;
-                    if constexpr (FP8) *(u32x4_t*)(vd + 16) = v1;
-                } else {
-                    char* kd = dst + row0 * KP * 2 + lane_koff;
-                    *(u32x4_t*)kd = v0;
-                    if constexpr (FP8) *(u32x4_t*)(kd + 16) = v1;
+                    *(u32x4_t*)d = st.c[k];
                 }
             }
         };
@@ -1138,10 +1128,10 @@ __global__ __launch_bounds__(64 * WR * TG, (D == 64 || NBW == 1 || TG > 1) ? 2 :
             issue(st[j], j);
             __builtin_amdgcn_sched_barrier(0);
         }
-        store(st[0], 0, 0);
+        store(st[0], 0);
         issue(st[0], DR);
         __builtin_amdgcn_sched_barrier(0);
-        store(st[1], 1, 1);
+        store(st[1], 1);
         issue(st[1], DR + 1);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
@@ -1183,7 +1173,7 @@ __global__ __launch_bounds__(64 * WR * TG, (D == 64 || NBW == 1 || TG > 1) ? 2 :
                         }
                     }
                 }
-                store(st[(j + 2) % DR], t + 2, slot2);
+                store(st[(j + 2) % DR], slot2);
                 issue(st[(j + 2) % DR], t + 2 + DR);
                 __builtin_amdgcn_sched_barrier(0);
                 __syncthreads();
