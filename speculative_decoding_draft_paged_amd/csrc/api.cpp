@@ -202,6 +202,15 @@ KernelShape choose_shape(int D, int NB, int R, int waves_override, long total_ti
         s.row_waves = (NB + s.nbw - 1) / s.nbw;
         s.all_on = NB % s.nbw == 0;
         s.waves_per_simd = s.nbw == 1 ? 2 : 1;
+        if (NB == 3 && waves_override == 0) {
+            // A fourth wave with no rows: each of the four 16-row halves of a K or V tile
+            // is then moved by one wave through one buffer resource, and two workgroups
+            // fill all four SIMDs twice. Measured against three waves: 7 % less per call
+            // at 1 and 8 requests of 16K keys, 0-1 % less at 64 requests and on the mixed
+            // batch (2 % with fp8 pools).
+            s.row_waves = 4;
+            s.all_on = false;
+        }
     } else if (waves_override > 0 && !s.shared) {
         s.token_groups = std::max(1, std::min(waves_override, max_waves / s.row_waves));
     }

@@ -102,7 +102,9 @@ def test_tile_kernel_choice():
     w = dict(head_dim=128, page_size=64, num_q_heads=16, num_kv_heads=1, window_left=4096)
     info = plan_info(params(**w, block_size=5), [8197, 8197])  # R = 80: one row block per wave
     assert info["shared_tiles"] == 1 and info["row_waves"] == 5 and info["token_groups"] == 1
-    info = plan_info(params(**w, block_size=3), [8195, 8195])  # R = 48: one block per wave as well
+    info = plan_info(params(**w, block_size=3), [8195, 8195])  # R = 48: one block per wave, plus a rowless wave
+    assert info["shared_tiles"] == 1 and info["row_waves"] == 4 and info["waves_per_unit"] == 4
+    info = plan_info(params(**w, block_size=3, waves_override=3), [8195, 8195])  # three waves, no rowless one
     assert info["shared_tiles"] == 1 and info["row_waves"] == 3
     info = plan_info(params(**w, block_size=3, waves_override=2), [8195, 8195])  # two blocks per wave
     assert info["shared_tiles"] == 1 and info["row_waves"] == 2

@@ -110,12 +110,12 @@ def test_split_invariance_shared_tiles(splits, waves, groups):
 
 
 @pytest.mark.parametrize("K,waves,row_waves,groups",
-                         [(7, 4, 4, 1), (5, 3, 3, 1), (3, 3, 3, 1), (3, 2, 2, 1), (3, 0, 3, 1), (7, 7, 7, 1),
+                         [(7, 4, 4, 1), (5, 3, 3, 1), (3, 3, 3, 1), (3, 2, 2, 1), (3, 0, 4, 1), (7, 7, 7, 1),
                           (7, 8, 4, 2), (7, 0, 7, 1), (8, 0, 8, 1), (4, 0, 4, 1)])
 def test_rows_per_wave_variants(K, waves, row_waves, groups):
     """Every row-blocks-per-wave choice of the shared-tile kernel at D = 128 meets the bar,
     with one token group or two (seven or eight row blocks); four row-waves load one
-    16-row half of K or V each."""
+    16-row half of K or V each (at three row blocks the fourth wave owns no rows)."""
     c = case(37 + K, batch=2, K=K, hq=16, hkv=1, D=128, P=64, ctx=2500, wl=1000, wr=-1)
     inp = synth.make_inputs(c)
     ref_out, ref_lse = oracle.attention_case(inp)
