@@ -1153,7 +1153,9 @@ __global__ __launch_bounds__(64 * WR * TG, (D == 64 || NBW == 1 || TG > 1) ? 2 :
                 constexpr bool kSwap = DR % 2 == 0;
                 f32x4_t(&s_cur)[NBW][2] = sbuf[kSwap ? (j & 1) : 0];
                 f32x4_t(&s_next)[NBW][2] = sbuf[kSwap ? ((j + 1) & 1) : 1];
-                if (t < nk) {
+                // A wave whose one row block holds no live rows only loads (the fourth wave
+                // at three row blocks).
+                if (t < nk && (ALL_ON || NBW > 1 || w.on[0])) {
                     // exponent arguments of tile t, then in one straight run the scores of
                     // tile t + 1 (past the end: zeros, unused) and the probabilities and PV
                     // product of tile t (a block with no live rows computes too: no branch)
