@@ -1025,9 +1025,11 @@ __global__ __launch_bounds__(64 * WR * TG, (D == 64 || NBW == 1 || TG > 1) ? 2 :
         // A tile is NBLK blocks of 64 16-byte pieces in four parts (K rows 0-15,
         // K rows 16-31, V rows 0-15, V rows 16-31) of BP blocks each. Row-wave w moves
         // blocks w, w + WR, ..., so each block's part, page and bases are wave-uniform
-        // scalars and a lane's offset inside a block is fixed. A wave's slot past the last
-        // block, and every block of a tile past the unit's end, reads through an empty
-        // buffer resource (zeros, no memory traffic) and is not stored.
+        // scalars and a lane's offset inside a block is fixed (with four row-waves, wave w
+        // moves the BP blocks of part w instead). A wave's slot past the last block, and
+        // every block of a tile past the unit's end, reads through an empty buffer
+        // resource (zeros, no memory traffic) and is not stored; every resource ends at
+        // the unit's last cached row, so rows past it load as zeros too.
         auto issue = [&](Stage& st, int t) {
             const bool real = t < nk;
             const int tc = real ? TG * t + tg : 0;  // window tile (any valid one when not real)

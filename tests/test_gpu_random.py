@@ -19,7 +19,7 @@ from tests import gpu_harness as H
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 96
+N_CASES = 256
 
 
 def draw(seed, max_rows=128):
@@ -92,7 +92,7 @@ def test_random_shape(seed):
     run_case(seed, 128)
 
 
-@pytest.mark.parametrize("seed", range(N_CASES, N_CASES + 24))
+@pytest.mark.parametrize("seed", range(N_CASES, N_CASES + 64))
 def test_random_shape_up_to_512_rows(seed):
     """Row groups: R up to 512 query rows per kv head."""
     run_case(seed, 512)
