@@ -1040,13 +1040,16 @@ __global__ __launch_bounds__(64 * WR * TG, (D == 64 || NBW == 1 || TG > 1) ? 2 :
                 const size_t slab = ((size_t)sl << (a.p_shift + kLog2<D>)) + (size_t)((t0 & pmask) * D);
                 // The resource ends at the last cached row: rows past it read as zeros (a
                 // V row there must not be a stale NaN; a K row there is masked anyway).
-                const int rows = real ? max(0, u.NC - t0) : 0;  // the loads touch only the part's BP KiB
+                // rows left from the part's first one; past 16 the part is whole (this also keeps
+                // the byte count far from overflow at any allowed length)
+                const int left = u.NC - t0;
+                const int bytes = !real ? 0 : (left >= 16 ? BP * 64 * 16 : max(0, left) * D * EB);
                 const uint64_t addr = reinterpret_cast<uint64_t>(pool_w) + slab * EB;
                 const char* base = reinterpret_cast<const char*>(
                     ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32)) << 32) |
                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)addr));
                 // (scalar operands: a resource built from vector registers needs a per-lane loop)
-                const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, __builtin_amdgcn_readfirstlane(rows * D * EB));
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, __builtin_amdgcn_readfirstlane(bytes));
 #pragma unroll
                 for (int k = 0; k < LPT; ++k)
                     st.c[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane_goff + k * 64 * 16, 0, kCachePolicyStream);
@@ -1065,11 +1068,11 @@ __global__ __launch_bounds__(64 * WR * TG, (D == 64 || NBW == 1 || TG > 1) ? 2 :
                 const int row0 = (part & 1) * 16 + (b % BP) * RPB;  // first tile row of the block
                 const char* base = static_cast<const char*>((part >> 1) ? a.vc : a.kc) +
                                    (((part & 1) ? slab1 : slab0) + (size_t)(b % BP) * RPB * D) * EB;
-                // the resource ends at the last cached row: rows past it read as zeros (the
-                // loads touch only the block's own 1 KiB, so a longer resource is harmless)
-                const int rows = (real && bw < NBLK) ? max(0, u.NC - (t0 + row0)) : 0;
-                st.c[k] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(base, rows * D * EB), lane_goff, 0,
-                                                                kCachePolicyStream);
+                // the resource ends at the last cached row: rows past it read as zeros (past
+                // RPB rows the block is whole)
+                const int left = u.NC - (t0 + row0);
+                const int bytes = !(real && bw < NBLK) ? 0 : (left >= RPB ? 64 * 16 : max(0, left) * D * EB);
+                st.c[k] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(base, bytes), lane_goff, 0, kCachePolicyStream);
             }
         };
         auto store = [&](Stage& st, int slot) {
