@@ -480,9 +480,9 @@ __device__ __forceinline__ void store_rows(const KernelArgs& a, const Unit& u, i
     if (quad == 0 && a.lse) a.lse[orow] = l == 0.f ? kNegInf : m + log2f(l);  // a NaN sum stays NaN
 }
 
-// Floats of LDS the in-kernel combine needs for S splits of R rows: the arrival flag, per-row
-// maximum and weight sum, and each split's exponent and weight sum per row.
-__host__ __device__ constexpr size_t last_arriver_floats(int S, int R) { return 4 + (size_t)2 * R + (size_t)2 * S * R; }
+// Floats of LDS the in-kernel combine needs for S splits of R rows: the arrival flag only (each
+// item folds its splits in registers).
+__host__ __device__ constexpr size_t last_arriver_floats(int S, int R) { return (void)S, (void)R, 4; }
 
 // The split combine inside the attention kernel, by the last unit of a (request, kv head,
 // row group) to finish (the multi-CTA split-KV of TensorRT-LLM PR #20374, Description: the
@@ -514,62 +514,42 @@ __device__ void combine_if_last(const KernelArgs& a, const Unit& u, float* lds) 
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
     const int u0 = blockIdx.x - u.s;  // the pair's units are consecutive
-    float* rowM = lds + 4;
-    float* rowL = rowM + R;
-    float* em = rowL + R;   // [S][R] exponents m_s, then weights 2^(m_s - M) / L
-    float* el = em + S * R;  // [S][R] weight sums l_s
-    // Row statistics: TPR threads per row, each folding every TPR-th split; the TPR threads of a
-    // row are consecutive lanes of one wave and meet by butterfly shuffles.
-    int tpr = 1;
-    while (tpr * 2 <= 64 && tpr * 2 * R <= nt) tpr *= 2;
-    const int r = tid / tpr, j = tid - (tid / tpr) * tpr;
-    const bool row_on = r < R;
-    float M = kNegInf;
-    if (row_on)
-        for (int s = j; s < S; s += tpr) {
-            const size_t pr = (size_t)(u0 + s) * R + r;
-            const float ms = ld_dev(a.part_m + pr), ls = ld_dev(a.part_l + pr);
-            em[s * R + r] = ms;
-            el[s * R + r] = ls;
-            M = fmaxf(M, ms);
-        }
-    for (int off = tpr >> 1; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-    float L = 0.f;
-    if (row_on)
-        for (int s = j; s < S; s += tpr) {
-            const float ms = em[s * R + r];
-            L += (ms == kNegInf ? 0.f : fast_exp2(ms - M)) * el[s * R + r];
-        }
-    for (int off = tpr >> 1; off > 0; off >>= 1) L += __shfl_xor(L, off, 64);
-    if (row_on) {
-        const float inv = L == 0.f ? 0.f : 1.f / L;  // no keys: zeros; a NaN sum stays NaN
-        for (int s = j; s < S; s += tpr) {
-            const float ms = em[s * R + r];
-            em[s * R + r] = (ms == kNegInf ? 0.f : fast_exp2(ms - M)) * inv;
-        }
-        if (j == 0) {
-            rowM[r] = M;
-            rowL[r] = L;
-        }
-    }
-    __syncthreads();
-    // Outputs: one float4 column of one row per item, summed over the splits in order. The pair's
-    // partials are S consecutive [R][D] blocks: one buffer resource covers them (byte offsets).
+    // One item per float4 column of a row. Each item folds the pair's S partials in split
+    // order into a running (m, l, acc) state, as the combine kernel does, so all of its loads
+    // are independent and issue together: one round trip from the last unit's arrival to its
+    // output. The partials are S consecutive [R] (m, l) and [R][D] (acc) blocks.
     const __amdgpu_buffer_rsrc_t accs = make_rsrc(a.part_acc + (size_t)u0 * R * D, (uint32_t)((size_t)S * R * D * 4));
+    const __amdgpu_buffer_rsrc_t mrs = make_rsrc(a.part_m + (size_t)u0 * R, (uint32_t)((size_t)S * R * 4));
+    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(a.part_l + (size_t)u0 * R, (uint32_t)((size_t)S * R * 4));
     for (int it = tid; it < R * DL; it += nt) {
         const int rr = it / DL, c = (it - (it / DL) * DL) * 4;
         const int rk = u.rg * R + rr;
         if (rk >= a.R_all) continue;
-        f32x4_t o = {0.f, 0.f, 0.f, 0.f};
-        const uint32_t base = (uint32_t)((rr * D + c) * 4), step = (uint32_t)(R * D * 4);
-#pragma unroll 16
-        for (int s = 0; s < S; ++s) o += ld_dev4(accs, base + (uint32_t)s * step) * em[s * R + rr];
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        float m = kNegInf, l = 0.f;
+        const uint32_t abase = (uint32_t)((rr * D + c) * 4), astep = (uint32_t)(R * D * 4);
+#pragma unroll 8
+        for (int s = 0; s < S; ++s) {
+            const uint32_t so = (uint32_t)((s * R + rr) * 4);
+            const float ms = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(mrs, so, 0, kCachePolicyDevice));
+            const float ls = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, so, 0, kCachePolicyDevice));
+            const f32x4_t as = ld_dev4(accs, abase + (uint32_t)s * astep);
+            // a split with no keys (m = -inf) weighs 0; 0 * NaN still carries a NaN sum through
+            const float mn = fmaxf(m, ms);
+            const float wa = m == kNegInf ? 0.f : fast_exp2(m - mn);
+            const float wb = ms == kNegInf ? 0.f : fast_exp2(ms - mn);
+            acc = acc * wa + as * wb;
+            l = l * wa + ls * wb;
+            m = mn;
+        }
+        const float inv = l == 0.f ? 0.f : 1.f / l;  // no keys: zeros; a NaN sum stays NaN
+        const f32x4_t o = acc * inv;
         const int i = rk / a.g, h = u.hk * a.g + (rk - (rk / a.g) * a.g);
         const size_t orow = (size_t)(u.b * a.K + i) * a.Hq + h;
         const uint32_t lo = f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
         const uint32_t hi = f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
         *(u32x2_t*)(a.out + orow * D + c) = u32x2_t{lo, hi};
-        if (c == 0 && a.lse) a.lse[orow] = rowL[rr] == 0.f ? kNegInf : rowM[rr] + log2f(rowL[rr]);
+        if (c == 0 && a.lse) a.lse[orow] = l == 0.f ? kNegInf : m + log2f(l);
     }
 }
 
