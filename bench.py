@@ -624,7 +624,8 @@ def main():
     ap.add_argument("--cases", default="128k",
                     help="per-case array in the same line: '128k' (the ten 128K-context cases, default), 'all', "
                          "'none', or a comma-separated list of case names")
-    ap.add_argument("--case-steps", type=int, default=20, help="calls per timed run for the per-case array")
+    ap.add_argument("--case-steps", type=int, default=50,
+                    help="calls per timed run for the per-case array (the headline's count by default)")
     ap.add_argument("--no-read-reference", action="store_true", help="skip the read-only 2 GiB streaming reference")
     ap.add_argument("--phase-trace", type=int, default=0, metavar="CALLS",
                     help="also trace CALLS eager calls of each timed case (per-unit phase timestamps) and report "
