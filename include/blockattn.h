@@ -89,10 +89,12 @@ typedef struct blockattn_params {
     int32_t waves_override;    /* 0: automatic. > 0: wavefronts per workgroup (1..8): token groups when
                                   R <= 32, row-waves (one or two row blocks each) when R > 32; at
                                   D = 128 with seven or eight 16-row blocks, a count above the block
-                                  count selects two token groups of four two-block waves (tuning).
-                                  Automatic at D = 128: two token groups for seven or eight blocks once
-                                  the batch holds at least 8 tiles per CU; four waves (one rowless) at
-                                  three blocks */
+                                  count selects two token groups of four two-block waves, and with
+                                  three blocks two token groups of four one-block waves, one of them
+                                  rowless (tuning). Automatic at D = 128: two token groups for seven
+                                  or eight blocks once the batch holds at least 8 tiles per CU; four
+                                  waves (one rowless) at three blocks, as two token groups with fp8
+                                  pools once the batch holds at least 64 tiles per CU */
     int32_t kv_dtype;          /* element type of k_cache and v_cache: BLOCKATTN_KV_BF16, or
                                   BLOCKATTN_KV_FP8_E4M3 (OCP fp8 E4M3 bytes: 1 sign, 4 exponent bits
                                   with bias 7, 3 mantissa bits, S.1111.111 = NaN; TensorRT-LLM PR #16150,

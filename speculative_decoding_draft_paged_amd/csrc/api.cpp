@@ -152,7 +152,7 @@ int tiles_for(const blockattn_params* p, int n) {
     return (n + kTileTokens - 1) / kTileTokens - lo / kTileTokens;
 }
 
-KernelShape choose_shape(int D, int NB, int R, int waves_override, long total_tiles) {
+KernelShape choose_shape(int D, int NB, int R, int waves_override, long total_tiles, bool fp8) {
     // Each wave owns up to two 16-row blocks of the R query rows. With one row-wave
     // (R <= 32), WT token groups of the workgroup stream different tiles, each wave
     // loading its own (stream_kernel). With WR > 1 row-waves the workgroup loads each
@@ -194,22 +194,29 @@ KernelShape choose_shape(int D, int NB, int R, int waves_override, long total_ti
         // windowed mixed batch: at three row blocks, three waves of one block beat two
         // waves of two (121 against 138 us per call); at seven, seven waves beat four
         // (151 against 197 us). waves_override picks the waves per workgroup: rows per
-        // wave = ceil(blocks / waves), 1 or 2; above the row blocks (seven or more), the
-        // two token groups.
+        // wave = ceil(blocks / waves), 1 or 2; above the row blocks (three, or seven or
+        // more), two token groups.
         int wv = NB;
         if (waves_override > 0) wv = std::max((NB + 1) / 2, std::min(waves_override, NB));
         s.nbw = (NB + wv - 1) / wv;
         s.row_waves = (NB + s.nbw - 1) / s.nbw;
         s.all_on = NB % s.nbw == 0;
         s.waves_per_simd = s.nbw == 1 ? 2 : 1;
-        if (NB == 3 && waves_override == 0) {
+        if (NB == 3 && (waves_override == 0 || waves_override > NB)) {
             // A fourth wave with no rows: each of the four 16-row halves of a K or V tile
-            // is then moved by one wave through one buffer resource, and two workgroups
-            // fill all four SIMDs twice. Measured against three waves: 7 % less per call
-            // at 1 and 8 requests of 16K keys, 0-1 % less at 64 requests and on the mixed
-            // batch (2 % with fp8 pools).
+            // is then moved by one wave through one buffer resource. Measured against three
+            // waves: 7 % less per call at 1 and 8 requests of 16K keys, 0-1 % less at 64
+            // requests and on the mixed batch (2 % with fp8 pools).
             s.row_waves = 4;
             s.all_on = false;
+            // fp8 pools with at least 64 tiles per CU (or a count above the blocks): two
+            // token groups of these four waves. The loading waves also widen the keys and
+            // values there, and one wave per SIMD leaves nothing to overlap that with; on
+            // the mixed batch at K = 3 this took 72 against 90 us per call. bf16 pools keep
+            // one group (85 against 88 us), as do smaller batches (64 requests of 2K keys
+            // with fp8 pools: 24.1 against 25.3 us).
+            if (waves_override > NB || (waves_override == 0 && fp8 && total_tiles >= 64L * kNumCUs))
+                s.token_groups = 2;
         }
     } else if (waves_override > 0 && !s.shared) {
         s.token_groups = std::max(1, std::min(waves_override, max_waves / s.row_waves));
@@ -244,7 +251,7 @@ int build_plan(const blockattn_params* p, const int32_t* lens, blockattn_plan_s*
         nt[b] = tiles_for(p, lens[b]);
         total += (long)nt[b] * H;
     }
-    pl->shape = choose_shape(p->head_dim, pl->NB, pl->R, p->waves_override, total);
+    pl->shape = choose_shape(p->head_dim, pl->NB, pl->R, p->waves_override, total, p->kv_dtype == BLOCKATTN_KV_FP8_E4M3);
     pl->shape.fp8 = p->kv_dtype == BLOCKATTN_KV_FP8_E4M3;
     // Workgroups resident per CU, from the kernel's waves per SIMD and its LDS.
     const int waves = pl->shape.row_waves * pl->shape.token_groups;
@@ -253,9 +260,12 @@ int build_plan(const blockattn_params* p, const int32_t* lens, blockattn_plan_s*
     wg_per_cu = std::max(1, std::min(wg_per_cu, waves_per_cu / waves));
     const long slots = (long)kNumCUs * wg_per_cu;
     // Tiles per unit (at least two per token group): the value that minimises an
-    // estimate of the makespan. Units run in rounds of `slots` resident workgroups; a
-    // round costs its largest unit's tiles plus a fixed start-up and epilogue cost,
-    // and splitting any request adds the combine launch. Both costs are in tiles.
+    // estimate of the makespan, in tiles. Workgroups resident on one CU share its
+    // throughput, so the tiles cost the largest unit's count once per unit a CU
+    // receives (units / CUs, rounded up), whether they run side by side or one after
+    // another. The fixed start-up and epilogue cost is paid once per round of `slots`
+    // resident workgroups (co-resident units overlap theirs), and splitting any request
+    // adds the combine launch.
     constexpr long kUnitCost = 8, kCombineCost = 8;
     const long wt = pl->shape.token_groups;
     long max_nt = 1;
@@ -272,7 +282,8 @@ int build_plan(const blockattn_params* p, const int32_t* lens, blockattn_plan_s*
                 largest = std::max(largest, (nt[b] + S - 1) / S);
                 split = split || S > 1;
             }
-            const long cost = (units + slots - 1) / slots * (largest + kUnitCost) + (split ? kCombineCost : 0);
+            const long cost = (units + kNumCUs - 1) / kNumCUs * largest + (units + slots - 1) / slots * kUnitCost +
+                              (split ? kCombineCost : 0);
             if (best < 0 || cost < best_cost) {
                 best = pu;
                 best_cost = cost;

@@ -1404,6 +1404,7 @@ hipError_t dispatch(const KernelShape& s, int units, const KernelArgs& args, hip
         BA_SHARED(128, 2, 4, 2)
         BA_SHARED1(128, 3)
         BA_SHARED(128, 1, 4, 1)
+        BA_SHARED(128, 1, 4, 2)
         BA_SHARED1(128, 5)
         BA_SHARED1(128, 6)
         BA_SHARED1(128, 7)

@@ -94,6 +94,36 @@ def test_two_token_groups_for_many_row_blocks_and_tiles():
     assert info["token_groups"] == 1 and info["row_waves"] == 5
 
 
+def test_three_blocks_two_token_groups_with_fp8_pools_and_many_tiles():
+    """Three row blocks at D = 128 (R = 48): four one-block waves, one rowless. With fp8 pools
+    and at least 64 tiles per CU (16384 tiles) they run as two token groups; bf16 pools and
+    smaller batches keep one group; a wave count above the blocks forces two groups."""
+    w = dict(head_dim=128, page_size=64, num_q_heads=64, num_kv_heads=4, block_size=3, window_left=4096,
+             window_right=-1, page_table_stride=300, num_pages=64 * 300)
+    n = 16384 + 3  # 129 window tiles per (request, kv head)
+    fp8_big = plan_info(params(**w, batch=32, kv_dtype="fp8_e4m3"), [n] * 32)    # 16512 tiles
+    fp8_small = plan_info(params(**w, batch=31, kv_dtype="fp8_e4m3"), [n] * 31)  # 15996 tiles
+    bf16_big = plan_info(params(**w, batch=32), [n] * 32)
+    forced = plan_info(params(**w, batch=2, waves_override=8), [n] * 2)
+    assert fp8_big["token_groups"] == 2 and fp8_big["row_waves"] == 4 and fp8_big["waves_per_unit"] == 8
+    for info in (fp8_small, bf16_big):
+        assert info["token_groups"] == 1 and info["row_waves"] == 4 and info["waves_per_unit"] == 4
+    assert forced["token_groups"] == 2 and forced["row_waves"] == 4
+
+
+def test_co_resident_workgroups_share_a_cu_in_the_split_choice():
+    """Four one-block waves at R = 48 fit two workgroups on a CU, but those share the CU's
+    throughput: 64 requests of 129 tiles take one unit per CU (4 splits, 256 units), not
+    two (8 splits, 512 units), and the mixed-length windowed batch keeps its requests whole."""
+    w = dict(head_dim=128, page_size=64, num_q_heads=16, num_kv_heads=1, block_size=3, window_left=4096,
+             window_right=-1, page_table_stride=300, num_pages=64 * 300)
+    info = plan_info(params(**w, batch=64), [16384 + 3] * 64)
+    assert info["units"] == 256 and info["max_splits"] == 4
+    lens = [2048 + 3 + (i * 977) % 14337 for i in range(64)]
+    info = plan_info(params(**dict(w, num_q_heads=64, num_kv_heads=4), batch=64), lens)
+    assert info["units"] == 256 and info["max_splits"] == 1
+
+
 def test_tile_kernel_choice():
     # R <= 32: one row-wave, waves stream their own tiles; more rows share tiles through LDS
     assert plan_info(params(), [5000, 5000])["shared_tiles"] == 0
@@ -275,10 +305,10 @@ def test_combine_mode_plan_choice():
     # one split per request: nothing to combine, whatever the mode
     one = plan_info(params(page_table_stride=4200, combine="last_arriver", splits_override=1), lens)
     assert one["fused_combine"] == 0 and one["combine_launch"] == 0
-    # the in-kernel combine keeps every split's statistics in LDS: too many splits are refused
-    with pytest.raises(ba.BlockAttnError) as e:
-        ba.blockattn_plan(params(page_table_stride=4200, combine="last_arriver", splits_override=4000), lens)
-    assert e.value.status == ba.BLOCKATTN_ERR_UNSUPPORTED and "LDS" in e.value.message
+    # the in-kernel combine folds each item's splits in registers (only its arrival flag sits in
+    # LDS), so any split count is accepted
+    many = plan_info(params(page_table_stride=4200, combine="last_arriver", splits_override=4000), lens)
+    assert many["fused_combine"] == 1 and many["max_splits"] == 4000
     with pytest.raises(ba.BlockAttnError) as e:
         ba.blockattn_plan(params(combine=3), [100, 100])
     assert e.value.status == ba.BLOCKATTN_ERR_INVALID_ARGUMENT and "combine_mode" in e.value.message

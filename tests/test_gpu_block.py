@@ -164,13 +164,16 @@ def test_fused_append_stores_the_encoded_block(idx, kw):
     H.compare(out2, lse2, ref2_out, ref2_lse, label=f"after append bk{idx}")
 
 
-# Seven and eight row blocks at D = 128 as two token groups (waves_override 8 or a large batch):
+# Seven and eight (or three) row blocks at D = 128 as two token groups (waves_override 8 or a large batch):
 # the block tile is consumed by the first group only, the append by every wave.
 TWO_GROUPS = [
     (30, dict(batch=2, K=7, hq=16, hkv=1, D=128, P=64, ctx=2500, wl=1000, wr=-1), 8, False),
     (31, dict(fp8=True, batch=3, K=7, hq=16, hkv=1, D=128, P=32, ctx_range=(0, 900)), 8, True),
     (32, dict(batch=2, K=7, hq=32, hkv=2, D=128, P=64, ctx=1300, wl=700, wr=2), 8, True),
     (33, dict(batch=16, K=8, hq=16, hkv=1, D=128, P=64, ctx=4100, wl=4096, wr=-1), 0, False),
+    # three row blocks: two groups of four one-block waves, one rowless
+    (34, dict(fp8=True, batch=3, K=3, hq=16, hkv=1, D=128, P=32, ctx_range=(0, 900)), 8, True),
+    (35, dict(batch=2, K=3, hq=32, hkv=2, D=128, P=64, ctx=1300, wl=700, wr=2), 8, False),
 ]
 
 

@@ -59,6 +59,18 @@ def test_last_arriver_combine_matches_oracle_and_kernel_combine(idx, kw, splits)
     print(f"cb{idx}: last arriver {rf}, kernel {rk}, splits {info_f['max_splits']}", flush=True)
 
 
+def test_last_arriver_with_two_token_groups_of_one_block_waves():
+    """Three row blocks as two token groups (one rowless wave each): the groups merge in LDS,
+    then the last split of each pair combines the pair's partials."""
+    c = ccase(11, fp8=True, batch=2, K=3, hq=16, hkv=1, D=128, P=64, ctx=5000, wl=3000, wr=-1)
+    inp = synth.make_inputs(c)
+    dc = H.upload(inp)
+    ref_out, ref_lse = oracle.attention_case(inp)
+    out_f, lse_f, info_f = H.run(dc, splits=6, waves=8, combine="last_arriver", canary=True)
+    assert info_f["fused_combine"] == 1 and info_f["token_groups"] == 2 and info_f["row_waves"] == 4
+    H.compare(out_f, lse_f, ref_out, ref_lse, label="cb11 last arriver, two groups")
+
+
 def test_last_arriver_with_empty_splits():
     """Device lengths far shorter than the plan's leave some splits with no tiles (m = -inf, l = 0)."""
     c = ccase(20, batch=2, ctx=8000)

@@ -60,6 +60,18 @@ def test_fp8_small(idx, kw):
     check_full(case8(idx, **kw), f"fp8 f{idx}")
 
 
+def test_fp8_three_blocks_two_token_groups():
+    """R = 48 with fp8 pools: two token groups of four one-block waves (one rowless), chosen
+    automatically once the batch holds at least 64 tiles per CU (here 256 (request, kv head)
+    pairs of 129 window tiles), and forced on a small ragged batch with forced splits."""
+    big = case8(30, batch=64, K=3, hq=64, hkv=4, D=128, P=64, ctx_range=(4200, 5000), wl=4096, wr=-1, outliers=0.01)
+    _, _, info = check_full(big, "fp8 f30")
+    assert info["token_groups"] == 2 and info["row_waves"] == 4 and info["max_splits"] == 1
+    small = case8(31, batch=3, K=3, hq=16, hkv=1, D=128, P=32, ctx_range=(0, 1800), ks=0.5, vs=2.0)
+    _, _, info = check_full(small, "fp8 f31", waves=8, splits=3)
+    assert info["token_groups"] == 2 and info["row_waves"] == 4
+
+
 @pytest.mark.parametrize("splits", [1, 3, 1000])
 def test_fp8_split_invariance(splits):
     c = case8(30, batch=2, K=7, hq=8, hkv=2, D=64, P=32, ctx=3000)

@@ -143,6 +143,23 @@ def test_two_token_groups(idx, kw, waves):
     check_full(case(idx, **kw), f"groups_{idx} splits=3", waves=waves, splits=3)
 
 
+# Three row blocks (R = 48) as two token groups of four one-block waves, one of them
+# rowless: forced here with a wave count above the blocks (automatic for fp8 pools of
+# at least 64 tiles per CU, covered in the fp8 tests).
+TWO_GROUPS_3 = [
+    (95, dict(batch=3, K=3, hq=16, hkv=1, D=128, P=32, ctx_range=(0, 2000))),                 # unwindowed, ragged
+    (96, dict(batch=2, K=3, hq=32, hkv=2, D=128, P=128, ctx=3333, wl=1500, wr=1)),            # W_r = 1
+    (97, dict(batch=2, K=3, hq=16, hkv=1, D=128, P=16, ctx_range=(100, 2500), wl=64, wr=-1)),  # short window
+]
+
+
+@pytest.mark.parametrize("idx,kw", TWO_GROUPS_3, ids=[f"groups3_{i}" for i, _ in TWO_GROUPS_3])
+def test_two_token_groups_three_blocks(idx, kw):
+    _, _, info = check_full(case(idx, **kw), f"groups3_{idx}", waves=8)
+    assert info["token_groups"] == 2 and info["row_waves"] == 4 and info["waves_per_unit"] == 8
+    check_full(case(idx, **kw), f"groups3_{idx} splits=5", waves=8, splits=5)
+
+
 def test_empty_splits_from_shorter_live_lengths():
     """Plan with long host lengths, run with shorter device lengths: trailing splits get no tiles."""
     c = case(31, batch=2, K=3, hq=4, hkv=1, D=64, P=32, ctx=2000)
