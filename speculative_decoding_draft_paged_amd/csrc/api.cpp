@@ -259,7 +259,11 @@ int build_plan(const blockattn_params* p, const int32_t* lens, blockattn_plan_s*
     int wg_per_cu = (int)std::max<size_t>(1, kLdsPerCU / std::max<size_t>(pl->shape.lds_bytes, 1));
     wg_per_cu = std::max(1, std::min(wg_per_cu, waves_per_cu / waves));
     const long slots = (long)kNumCUs * wg_per_cu;
-    // Tiles per unit (at least two per token group): the value that minimises an
+    // Tiles per unit (at least two per wave of the streaming kernel at D = 64 and one at
+    // D = 128, 16 KiB of bf16 keys and values either way: one D = 128 tile per wave took
+    // 5-10 % off the windowed K = 1 batches of 1 and 8 requests, one D = 64 tile per wave
+    // added 4-7 % at one 32K request; two for the shared-tile kernel, whose prologue
+    // stages two tiles): the value that minimises an
     // estimate of the makespan, in tiles. Workgroups resident on one CU share its
     // throughput, so the tiles cost the largest unit's count once per unit a CU
     // receives (units / CUs, rounded up), whether they run side by side or one after
@@ -270,7 +274,7 @@ int build_plan(const blockattn_params* p, const int32_t* lens, blockattn_plan_s*
     const long wt = pl->shape.token_groups;
     long max_nt = 1;
     for (int b = 0; b < B; ++b) max_nt = std::max<long>(max_nt, nt[b]);
-    long per_unit = std::max(2 * wt, (total + slots - 1) / slots);
+    long per_unit = std::max(pl->shape.shared ? 2 : (p->head_dim == 64 ? 2 : 1) * wt, (total + slots - 1) / slots);
     if (p->splits_override <= 0 && per_unit < max_nt) {
         long best = -1, best_cost = 0;
         for (long pu = per_unit;; pu = std::min(max_nt, std::max(pu + 1, pu * 9 / 8))) {

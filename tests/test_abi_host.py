@@ -124,6 +124,17 @@ def test_co_resident_workgroups_share_a_cu_in_the_split_choice():
     assert info["units"] == 256 and info["max_splits"] == 1
 
 
+def test_streaming_units_hold_16k_of_keys_and_values_per_wave():
+    """The split choice's floor: two 32-token tiles per wave at D = 64 (eight waves: 16
+    tiles per unit), one at D = 128 (four waves: 4 tiles per unit)."""
+    d128 = dict(head_dim=128, page_size=64, num_q_heads=16, num_kv_heads=1, block_size=1, window_left=4096,
+                window_right=-1, page_table_stride=300, num_pages=300)
+    info = plan_info(params(**d128, batch=1), [16384 + 1])  # 129 window tiles
+    assert info["shared_tiles"] == 0 and info["max_splits"] == 33
+    info = plan_info(params(page_table_stride=1100, batch=1), [32768 + 7])  # 1025 tiles at D = 64
+    assert info["shared_tiles"] == 0 and info["max_splits"] == 65
+
+
 def test_tile_kernel_choice():
     # R <= 32: one row-wave, waves stream their own tiles; more rows share tiles through LDS
     assert plan_info(params(), [5000, 5000])["shared_tiles"] == 0
