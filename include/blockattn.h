@@ -110,8 +110,8 @@ typedef struct blockattn_params {
                                   BLOCKATTN_COMBINE_LAST_ARRIVER (2) has the last split of each
                                   (request, kv head) to finish combine them inside the attention kernel,
                                   found by a per-(request, kv head) arrival counter in the workspace
-                                  (refused with BLOCKATTN_ERR_UNSUPPORTED when the split statistics do not
-                                  fit the kernel's LDS) */
+                                  (any split count; that unit reads every partial of its pair, so it
+                                  pays off only at few, narrow splits) */
 } blockattn_params;
 
 enum { BLOCKATTN_COMBINE_AUTO = 0, BLOCKATTN_COMBINE_KERNEL = 1, BLOCKATTN_COMBINE_LAST_ARRIVER = 2 };

@@ -7,10 +7,10 @@
 // split-KV), and the split count of the paged split-KV kernel (PR #16150, commit
 // list: a flash-decoding style rework whose split count became a runtime
 // argument). Here one kernel covers every batch: the plan picks the tiles per
-// split that minimise an estimated makespan over the workgroups the 256 gfx950
-// compute units hold at once (rounds of resident units, a fixed cost per unit,
-// and the combine launch when any request is split), so every split keeps enough
-// keys that its fp32 partial state stays small next to the KV bytes it reads. The workspace is
+// split that minimise an estimated makespan on the 256 gfx950 compute units (each
+// CU's tiles at its own rate, a fixed cost per round of resident units, and the
+// combine launch when any request is split), so every split keeps enough keys that
+// its fp32 partial state stays small next to the KV bytes it reads. The workspace is
 // sized exactly and checked before anything launches, the lesson of PR #21130's
 // workspace item 3 (a stats carve that outgrew its buffer).
 #include "blockattn.h"
@@ -324,16 +324,9 @@ int build_plan(const blockattn_params* p, const int32_t* lens, blockattn_plan_s*
     // pair's partials through device-scope loads while the combine kernel spreads them over
     // many workgroups.
     pl->fused = false;
-    if (pl->max_splits > 1 && p->combine_mode == BLOCKATTN_COMBINE_LAST_ARRIVER) {
-        if (last_arriver_lds_floats(pl->max_splits, pl->R) * sizeof(float) > pl->shape.lds_bytes) {
-            char buf[200];
-            snprintf(buf, sizeof buf,
-                     "the in-kernel combine of %d splits of %d rows needs more LDS than the kernel has; use "
-                     "BLOCKATTN_COMBINE_KERNEL or fewer splits", pl->max_splits, pl->R);
-            return fail(BLOCKATTN_ERR_UNSUPPORTED, buf);
-        }
-        pl->fused = true;
-    }
+    // (Its only LDS is one arrival flag, which every kernel shape has: each item folds its
+    // splits in registers.)
+    if (pl->max_splits > 1 && p->combine_mode == BLOCKATTN_COMBINE_LAST_ARRIVER) pl->fused = true;
 
     Layout& L = pl->lay;
     L.work = 0;

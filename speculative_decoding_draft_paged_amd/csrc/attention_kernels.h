@@ -480,10 +480,6 @@ __device__ __forceinline__ void store_rows(const KernelArgs& a, const Unit& u, i
     if (quad == 0 && a.lse) a.lse[orow] = l == 0.f ? kNegInf : m + log2f(l);  // a NaN sum stays NaN
 }
 
-// Floats of LDS the in-kernel combine needs for S splits of R rows: the arrival flag only (each
-// item folds its splits in registers).
-__host__ __device__ constexpr size_t last_arriver_floats(int S, int R) { return (void)S, (void)R, 4; }
-
 // The split combine inside the attention kernel, by the last unit of a (request, kv head,
 // row group) to finish (the multi-CTA split-KV of TensorRT-LLM PR #20374, Description: the
 // splits of a decode row meet through counter buffers). Every unit of a split pair has

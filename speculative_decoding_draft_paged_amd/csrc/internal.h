@@ -80,8 +80,6 @@ struct KernelShape {
 };
 
 size_t attention_lds_bytes(const KernelShape& s, int R);
-// Floats of LDS the in-kernel split combine needs for S splits of R rows.
-size_t last_arriver_lds_floats(int S, int R);
 
 hipError_t launch_attention(const KernelShape& shape, bool windowed, int units, const KernelArgs& args,
                             hipStream_t stream);

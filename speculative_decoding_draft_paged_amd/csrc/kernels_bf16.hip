@@ -52,8 +52,6 @@ size_t attention_lds_bytes(const KernelShape& s, int R) {
     return loop > epi ? loop : epi;
 }
 
-size_t last_arriver_lds_floats(int S, int R) { return last_arriver_floats(S, R); }
-
 hipError_t launch_attention(const KernelShape& shape, bool windowed, int units, const KernelArgs& args,
                             hipStream_t stream) {
     if (shape.fp8) return launch_attention_fp8(shape, windowed, units, args, stream);
