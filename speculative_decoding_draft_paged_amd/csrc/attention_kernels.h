@@ -1137,13 +1137,14 @@ __global__ __launch_bounds__(64 * WR * TG, (D == 64 || NBW == 1 || TG > 1) ? 2 :
                 // A wave whose one row block holds no live rows only loads (the fourth wave
                 // at three row blocks).
                 if (t < nk && (ALL_ON || NBW > 1 || w.on[0])) {
-                    // exponent arguments of tile t, then in one straight run the scores of
+                    // the keys of tile t + 1 from LDS first (their latency runs under the
+                    // exponent arguments of tile t), then in one straight run the scores of
                     // tile t + 1 (past the end: zeros, unused) and the probabilities and PV
                     // product of tile t (a block with no live rows computes too: no branch)
-                    float y[NBW][8];
-                    w.template prep<true>(s_cur, (win + TG * t + tg) * T, a.scale_log2, quad, y);
                     bf16x8_t kf[2][KK];
                     read_k(slot1, kf);
+                    float y[NBW][8];
+                    w.template prep<true>(s_cur, (win + TG * t + tg) * T, a.scale_log2, quad, y);
                     bf16x8_t vf[DB];
                     read_v(slot, vf);
                     w.template scores<true>(kf, s_next);
